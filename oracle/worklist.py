@@ -1,0 +1,70 @@
+"""Reference tile schedule for the coalesced launch (integer work).
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.
+
+The engine "stably schedules and fuses" whole sequences and shards on a
+shared rank (pith.science review of arXiv 2608.01150, "What carries the
+argument"). The pages give no algorithm; the reading taken here is a
+stable longest-processing-time-first (LPT) list schedule:
+
+1. Cut every item into tiles of ``block_m`` query rows x one head, in the
+   order (item, head, query block).
+2. Cost of a tile = rows * kv_len + c0 (c0: fixed per-tile overhead).
+3. Sort by cost, largest first; the sort is stable, so equal costs keep
+   the order of step 1.
+4. With n_slots > 0, give each tile in that order to the slot with the
+   least load so far (lowest slot index on ties). With n_slots == 0 the
+   sorted order itself is the schedule (one workgroup per tile).
+
+Python's ``sorted`` is stable and the slot search is a plain scan, so the
+result can be checked against the C++ builder bit for bit.
+"""
+
+from __future__ import annotations
+
+from typing import Iterable, List, NamedTuple, Tuple
+
+
+class Tile(NamedTuple):
+    q_row0: int
+    kv_row0: int
+    q_rows: int
+    kv_len: int
+    head: int
+    item: int
+    cost: int
+
+
+def cut_tiles(items: Iterable, block_m: int, c0: int) -> List[Tile]:
+    tiles = []
+    for idx, it in enumerate(items):
+        q_off, q_len, kv_off, kv_len, h0, hc = (it.as_tuple() if hasattr(it, "as_tuple")
+                                                else tuple(int(x) for x in it))
+        for h in range(h0, h0 + hc):
+            for r0 in range(0, q_len, block_m):
+                rows = min(block_m, q_len - r0)
+                tiles.append(Tile(q_off + r0, kv_off, rows, kv_len, h, idx,
+                                  rows * kv_len + c0))
+    return tiles
+
+
+def lpt_schedule(items: Iterable, block_m: int, n_slots: int, c0: int
+                 ) -> Tuple[List[Tile], List[int], List[int]]:
+    """Returns (tiles in schedule order, slot_begin offsets [n_slots+1],
+    slot loads). For n_slots == 0: (tiles in LPT order, [], [])."""
+    tiles = cut_tiles(items, block_m, c0)
+    order = sorted(tiles, key=lambda t: -t.cost)
+    if n_slots == 0:
+        return order, [], []
+    loads = [0] * n_slots
+    per_slot: List[List[Tile]] = [[] for _ in range(n_slots)]
+    for t in order:
+        s = min(range(n_slots), key=lambda i: (loads[i], i))
+        per_slot[s].append(t)
+        loads[s] += t.cost
+    flat, begin = [], [0]
+    for s in range(n_slots):
+        flat += per_slot[s]
+        begin.append(len(flat))
+    return flat, begin, loads

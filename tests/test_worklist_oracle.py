@@ -1,0 +1,81 @@
+"""Pins of the reference LPT schedule: coverage, stability, lower bounds and
+Graham's LPT bound against a brute-force optimum on tiny inputs."""
+
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle.worklist import cut_tiles, lpt_schedule
+
+
+def _items(rng, n):
+    out = []
+    q = kv = 0
+    for _ in range(n):
+        ql, kl = int(rng.integers(0, 400)), int(rng.integers(0, 500))
+        h0 = int(rng.integers(0, 3)); hc = int(rng.integers(1, 3))
+        out.append((q, ql, kv, kl, h0, hc))
+        q += ql; kv += kl
+    return out
+
+
+def test_cover_every_row_head_once():
+    rng = np.random.default_rng(0)
+    items = _items(rng, 12)
+    tiles, begin, loads = lpt_schedule(items, 128, 7, 64)
+    cov = {}
+    for t in tiles:
+        for r in range(t.q_row0, t.q_row0 + t.q_rows):
+            cov[(r, t.head)] = cov.get((r, t.head), 0) + 1
+    want = {(it[0] + r, h) for it in items for r in range(it[1]) for h in range(it[4], it[4] + it[5])}
+    assert set(cov) == want and set(cov.values()) == {1}
+    assert begin[0] == 0 and begin[-1] == len(tiles) and len(begin) == 8
+    assert loads == [sum(t.cost for t in tiles[begin[s]:begin[s + 1]]) for s in range(7)]
+
+
+def test_stable_order_and_determinism():
+    items = [(0, 256, 0, 300, 0, 2), (256, 256, 300, 300, 0, 2)]  # all tiles cost-equal
+    order, _, _ = lpt_schedule(items, 128, 0, 10)
+    assert [(t.item, t.head, t.q_row0) for t in order] == [
+        (0, 0, 0), (0, 0, 128), (0, 1, 0), (0, 1, 128), (1, 0, 256), (1, 0, 384), (1, 1, 256), (1, 1, 384)]
+    assert lpt_schedule(items, 128, 3, 10) == lpt_schedule(items, 128, 3, 10)
+    costs = [t.cost for t in lpt_schedule(_items(np.random.default_rng(1), 9), 64, 0, 5)[0]]
+    assert costs == sorted(costs, reverse=True)
+
+
+def _opt_makespan(costs, m):
+    best = float("inf")
+    for assign in itertools.product(range(m), repeat=len(costs)):
+        loads = [0] * m
+        for c, s in zip(costs, assign):
+            loads[s] += c
+        best = min(best, max(loads))
+    return best
+
+
+def test_graham_bound_against_brute_force():
+    rng = np.random.default_rng(2)
+    for trial in range(40):
+        m = int(rng.integers(2, 4))
+        n_items = int(rng.integers(1, 4))
+        items = []
+        q = 0
+        for i in range(n_items):
+            ql = int(rng.integers(1, 5)) * 32 - int(rng.integers(0, 31))
+            items.append((q, ql, 0, int(rng.integers(1, 90)), 0, 1))
+            q += ql
+        tiles = cut_tiles(items, 32, 3)
+        if len(tiles) > 10:
+            continue
+        _, _, loads = lpt_schedule(items, 32, m, 3)
+        opt = _opt_makespan([t.cost for t in tiles], m)
+        mk = max(loads)
+        assert mk >= opt and mk >= max(t.cost for t in tiles) and mk * m >= sum(t.cost for t in tiles)
+        assert mk <= (4 / 3 - 1 / (3 * m)) * opt + 1e-9
+
+
+def test_empty_and_zero_kv_items():
+    tiles, begin, loads = lpt_schedule([(0, 0, 0, 5, 0, 1), (0, 10, 0, 0, 0, 1)], 128, 2, 7)
+    assert len(tiles) == 1 and tiles[0].cost == 7 and tiles[0].kv_len == 0
+    assert loads == [7, 0]
