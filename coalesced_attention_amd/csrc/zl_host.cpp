@@ -1,0 +1,254 @@
+// Host half of libzl.so: status strings, thread-local error text, argument
+// validation and the stable LPT worklist builder. Plain C++17 with no HIP
+// headers, so it builds with hipcc for the library and with g++ (under
+// sanitizers) for host-only checks.
+//
+// Scheduling reading: the engine "stably schedules and fuses" whole
+// sequences and distributed-attention shards on a shared rank (pith.science
+// review of arXiv 2608.01150, "What carries the argument"). Tiles are cut
+// per (item, head, query block), sorted by cost with a total order that
+// keeps equal costs in cut order (a stable sort), and placed longest first
+// on the least-loaded slot.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "zl.h"
+#include "zl_internal.h"
+
+namespace zl {
+
+namespace {
+thread_local std::string g_error;
+}
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+void clear_error() { g_error.clear(); }
+
+int check_worklist(const void* h_wl, const zl_worklist_header** hdr) {
+  if (!h_wl) return fail(ZL_ERR_NULL, "host worklist is NULL");
+  const auto* h = static_cast<const zl_worklist_header*>(h_wl);
+  if (h->magic != ZL_WORKLIST_MAGIC) return fail(ZL_ERR_WORKLIST, "worklist magic mismatch");
+  if (h->abi_version != ZL_ABI_VERSION)
+    return fail(ZL_ERR_WORKLIST, "worklist built for ABI %u, library is %d", h->abi_version,
+                ZL_ABI_VERSION);
+  if ((h->head_dim != 64 && h->head_dim != 128) || h->num_heads < 1 || h->n_tiles < 0 ||
+      h->n_slots < 0 || h->n_slots > kMaxSlots || h->block_m != kFwdBlockM ||
+      !(h->softmax_scale > 0.f) || h->q_rows < 0 || h->kv_rows < 0)
+    return fail(ZL_ERR_WORKLIST, "worklist header fields out of range");
+  uint64_t need = h->tiles_offset + uint64_t(h->n_tiles) * sizeof(zl_tile);
+  if (h->n_slots > 0) {
+    if (h->slots_offset < need) return fail(ZL_ERR_WORKLIST, "worklist slot table overlaps tiles");
+    need = h->slots_offset + uint64_t(h->n_slots + 1) * sizeof(int32_t);
+  }
+  if (h->tiles_offset < sizeof(zl_worklist_header) || (h->tiles_offset & 15u) ||
+      (h->slots_offset & 15u) || need > h->total_bytes)
+    return fail(ZL_ERR_WORKLIST, "worklist offsets inconsistent with its size");
+  *hdr = h;
+  return ZL_OK;
+}
+
+}  // namespace zl
+
+using namespace zl;
+
+extern "C" int zl_abi_version(void) { return ZL_ABI_VERSION; }
+
+extern "C" const char* zl_status_string(int status) {
+  switch (status) {
+    case ZL_OK: return "ok";
+    case ZL_ERR_NULL: return "null pointer";
+    case ZL_ERR_SHAPE: return "unsupported shape";
+    case ZL_ERR_RANGE: return "item out of range";
+    case ZL_ERR_OVERLAP: return "items overlap";
+    case ZL_ERR_BUFSIZE: return "buffer too small";
+    case ZL_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case ZL_ERR_WORKLIST: return "invalid worklist";
+    case ZL_ERR_HIP: return "HIP error";
+    case ZL_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+extern "C" const char* zl_last_error(void) { return g_error.c_str(); }
+
+namespace {
+
+constexpr uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+int validate_items(const zl_problem& p, const zl_item* items, int32_t n_items) {
+  for (int32_t i = 0; i < n_items; ++i) {
+    const zl_item& it = items[i];
+    if (it.q_len < 0 || it.kv_len < 0 || it.head_cnt < 0 || it.q_off < 0 || it.kv_off < 0 ||
+        it.head_begin < 0)
+      return fail(ZL_ERR_RANGE, "item %d has a negative field", i);
+    if (it.q_off + it.q_len > p.q_rows || it.kv_off + it.kv_len > p.kv_rows ||
+        int64_t(it.head_begin) + it.head_cnt > p.num_heads)
+      return fail(ZL_ERR_RANGE, "item %d lies outside the packed buffers or heads", i);
+  }
+  // Two items may share query rows only on disjoint heads.
+  std::vector<int32_t> order;
+  order.reserve(n_items);
+  for (int32_t i = 0; i < n_items; ++i)
+    if (items[i].q_len > 0 && items[i].head_cnt > 0) order.push_back(i);
+  std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    return items[a].q_off != items[b].q_off ? items[a].q_off < items[b].q_off : a < b;
+  });
+  for (size_t x = 0; x < order.size(); ++x) {
+    const zl_item& a = items[order[x]];
+    for (size_t y = x + 1; y < order.size(); ++y) {
+      const zl_item& b = items[order[y]];
+      if (b.q_off >= a.q_off + a.q_len) break;
+      if (b.head_begin < a.head_begin + a.head_cnt && a.head_begin < b.head_begin + b.head_cnt)
+        return fail(ZL_ERR_OVERLAP, "items %d and %d write the same (row, head)", order[x],
+                    order[y]);
+    }
+  }
+  return ZL_OK;
+}
+
+struct TileKey {
+  zl_tile t;
+  int64_t cost;
+};
+
+}  // namespace
+
+extern "C" int zl_build_worklist(const zl_problem* problem, const zl_item* items, int32_t n_items,
+                                 int32_t n_slots, void* host_buf, size_t* bytes) {
+  clear_error();
+  if (!problem || !bytes) return fail(ZL_ERR_NULL, "problem and bytes must be non-NULL");
+  if (n_items < 0) return fail(ZL_ERR_ARG, "n_items < 0");
+  if (n_items > 0 && !items) return fail(ZL_ERR_NULL, "items is NULL");
+  if (n_slots < 0 || n_slots > kMaxSlots) return fail(ZL_ERR_ARG, "n_slots out of range");
+  const zl_problem& p = *problem;
+  if ((p.head_dim != 64 && p.head_dim != 128) || p.num_heads < 1 || p.q_rows < 0 ||
+      p.kv_rows < 0)
+    return fail(ZL_ERR_SHAPE, "head_dim must be 64 or 128 and sizes non-negative");
+  if (p.reserved != 0) return fail(ZL_ERR_ARG, "problem.reserved must be 0");
+  if (!(p.softmax_scale <= 0.f || std::isfinite(p.softmax_scale)))
+    return fail(ZL_ERR_ARG, "softmax_scale must be finite");
+  int rc = validate_items(p, items, n_items);
+  if (rc) return rc;
+
+  const int block_m = kFwdBlockM;
+  int64_t n_tiles64 = 0;
+  for (int32_t i = 0; i < n_items; ++i) {
+    const zl_item& it = items[i];
+    n_tiles64 += int64_t(it.head_cnt) * ((int64_t(it.q_len) + block_m - 1) / block_m);
+  }
+  if (n_tiles64 > INT32_MAX) return fail(ZL_ERR_ARG, "too many tiles");
+  const int32_t n_tiles = int32_t(n_tiles64);
+  const uint64_t tiles_off = align_up(sizeof(zl_worklist_header), 256);
+  const uint64_t slots_off = align_up(tiles_off + uint64_t(n_tiles) * sizeof(zl_tile), 256);
+  const uint64_t total = align_up(slots_off + (n_slots > 0 ? uint64_t(n_slots + 1) * 4 : 0), 256);
+  if (!host_buf) {
+    *bytes = size_t(total);
+    return ZL_OK;
+  }
+  if (*bytes < total) return fail(ZL_ERR_BUFSIZE, "worklist needs %llu bytes", (unsigned long long)total);
+  if (reinterpret_cast<uintptr_t>(host_buf) & 7u) return fail(ZL_ERR_ALIGN, "host_buf must be 8-byte aligned");
+
+  const int64_t c0 = int64_t(block_m) * kCostC0PerRow;
+  std::vector<TileKey> tiles;
+  try {
+    tiles.reserve(size_t(n_tiles));
+  } catch (const std::bad_alloc&) {
+    return fail(ZL_ERR_ARG, "out of host memory for %d tiles", n_tiles);
+  }
+  for (int32_t i = 0; i < n_items; ++i) {
+    const zl_item& it = items[i];
+    for (int32_t h = it.head_begin; h < it.head_begin + it.head_cnt; ++h)
+      for (int32_t r0 = 0; r0 < it.q_len; r0 += block_m) {
+        const int32_t rows = std::min(block_m, it.q_len - r0);
+        TileKey k;
+        k.t = zl_tile{it.q_off + r0, it.kv_off, rows, it.kv_len, h, i};
+        k.cost = int64_t(rows) * it.kv_len + c0;
+        tiles.push_back(k);
+      }
+  }
+  // Largest cost first; equal costs keep cut order (item, head, query row),
+  // which is a total order, so std::sort gives the stable result.
+  std::sort(tiles.begin(), tiles.end(), [](const TileKey& a, const TileKey& b) {
+    if (a.cost != b.cost) return a.cost > b.cost;
+    if (a.t.item != b.t.item) return a.t.item < b.t.item;
+    if (a.t.head != b.t.head) return a.t.head < b.t.head;
+    return a.t.q_row0 < b.t.q_row0;
+  });
+
+  char* base = static_cast<char*>(host_buf);
+  std::memset(base, 0, size_t(total));
+  auto* hdr = reinterpret_cast<zl_worklist_header*>(base);
+  auto* out = reinterpret_cast<zl_tile*>(base + tiles_off);
+  int64_t total_cost = 0, makespan = 0;
+  for (const TileKey& k : tiles) total_cost += k.cost;
+
+  if (n_slots == 0) {
+    for (int32_t t = 0; t < n_tiles; ++t) out[t] = tiles[size_t(t)].t;
+  } else {
+    // Least-loaded slot, lowest index on ties: a binary heap ordered by
+    // (load, slot). The chosen slot of each tile is kept in LPT order and
+    // the tiles are then laid out slot by slot (a stable counting sort).
+    std::vector<std::pair<int64_t, int32_t>> heap;
+    std::vector<int32_t> slot_of(static_cast<size_t>(n_tiles));
+    std::vector<int32_t> count(static_cast<size_t>(n_slots) + 1, 0);
+    std::vector<int64_t> load(size_t(n_slots), 0);
+    heap.reserve(size_t(n_slots));
+    for (int32_t s = 0; s < n_slots; ++s) heap.emplace_back(0, s);
+    auto cmp = [](const std::pair<int64_t, int32_t>& a, const std::pair<int64_t, int32_t>& b) {
+      return a > b;  // min-heap on (load, slot)
+    };
+    std::make_heap(heap.begin(), heap.end(), cmp);
+    for (int32_t t = 0; t < n_tiles; ++t) {
+      std::pop_heap(heap.begin(), heap.end(), cmp);
+      const int32_t s = heap.back().second;
+      heap.back().first += tiles[size_t(t)].cost;
+      slot_of[size_t(t)] = s;
+      load[size_t(s)] = heap.back().first;
+      ++count[size_t(s) + 1];
+      std::push_heap(heap.begin(), heap.end(), cmp);
+    }
+    for (int32_t s = 0; s < n_slots; ++s) count[size_t(s) + 1] += count[size_t(s)];
+    auto* slots = reinterpret_cast<int32_t*>(base + slots_off);
+    for (int32_t s = 0; s <= n_slots; ++s) slots[s] = count[size_t(s)];
+    std::vector<int32_t> fill(count.begin(), count.end() - 1);
+    for (int32_t t = 0; t < n_tiles; ++t) out[fill[size_t(slot_of[size_t(t)])]++] = tiles[size_t(t)].t;
+    for (int64_t l : load) makespan = std::max(makespan, l);
+  }
+
+  hdr->magic = ZL_WORKLIST_MAGIC;
+  hdr->abi_version = ZL_ABI_VERSION;
+  hdr->total_bytes = total;
+  hdr->q_rows = p.q_rows;
+  hdr->kv_rows = p.kv_rows;
+  hdr->num_heads = p.num_heads;
+  hdr->head_dim = p.head_dim;
+  hdr->softmax_scale = p.softmax_scale > 0.f ? p.softmax_scale
+                                             : float(1.0 / std::sqrt(double(p.head_dim)));
+  hdr->block_m = block_m;
+  hdr->n_items = n_items;
+  hdr->n_tiles = n_tiles;
+  hdr->n_slots = n_slots;
+  hdr->cost_c0 = int32_t(c0);
+  hdr->tiles_offset = tiles_off;
+  hdr->slots_offset = n_slots > 0 ? slots_off : 0;
+  hdr->total_cost = total_cost;
+  hdr->max_slot_cost = makespan;
+  *bytes = size_t(total);
+  return ZL_OK;
+}

@@ -1,0 +1,32 @@
+// Internal declarations shared by the host code and the HIP entry points of
+// libzl.so. Not part of the ABI.
+#ifndef ZL_INTERNAL_H_
+#define ZL_INTERNAL_H_
+
+#include <stdint.h>
+
+#include "zl.h"
+
+namespace zl {
+
+// Forward tile: 8 waves x 32 query rows (one 32-row MFMA block per wave).
+constexpr int kFwdWaves = 8;
+constexpr int kFwdBlockM = kFwdWaves * 32;
+// Per-tile fixed cost in (query row x key) units used by the LPT rule: the
+// prologue and epilogue of a tile cost about as much as 64 keys of work.
+constexpr int kCostC0PerRow = 64;
+// Largest static slot count accepted by zl_build_worklist.
+constexpr int kMaxSlots = 1 << 20;
+
+// Record a printf-style detail for zl_last_error() and return `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clear the thread-local error text.
+void clear_error();
+// Validate a host copy of a worklist; on success *hdr points into it.
+int check_worklist(const void* h_wl, const zl_worklist_header** hdr);
+// True if p is non-null and 16-byte aligned.
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace zl
+
+#endif  // ZL_INTERNAL_H_

@@ -1,0 +1,238 @@
+"""Thin Python binding over the C ABI of libzl.so (include/zl.h).
+
+Argument marshalling only: every step of the path runs in libzl.so. PyTorch
+provides device memory and the stream. Importing this module loads the
+library and raises ImportError if it has not been built; there is no
+fallback of any kind.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libzl.so")
+
+ZL_OK = 0
+STATUS = {0: "ZL_OK", -1: "ZL_ERR_NULL", -2: "ZL_ERR_SHAPE", -3: "ZL_ERR_RANGE",
+          -4: "ZL_ERR_OVERLAP", -5: "ZL_ERR_BUFSIZE", -6: "ZL_ERR_ALIGN",
+          -7: "ZL_ERR_WORKLIST", -8: "ZL_ERR_HIP", -9: "ZL_ERR_ARG"}
+WORKLIST_MAGIC = 0x31574C5A
+
+# Symbols include/zl.h declares (checked by the CPU tests).
+EXPORTS = ("zl_abi_version", "zl_status_string", "zl_last_error", "zl_build_worklist",
+           "zl_coalesced_attn_fwd", "zl_merge_partials")
+
+
+class ZlError(RuntimeError):
+    def __init__(self, code: int, where: str, detail: str):
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({detail})")
+        self.code = code
+
+
+class Item(ctypes.Structure):
+    _fields_ = [("q_off", ctypes.c_int64), ("kv_off", ctypes.c_int64),
+                ("q_len", ctypes.c_int32), ("kv_len", ctypes.c_int32),
+                ("head_begin", ctypes.c_int32), ("head_cnt", ctypes.c_int32)]
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("q_rows", ctypes.c_int64), ("kv_rows", ctypes.c_int64),
+                ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("reserved", ctypes.c_int32)]
+
+
+class Tile(ctypes.Structure):
+    _fields_ = [("q_row0", ctypes.c_int64), ("kv_row0", ctypes.c_int64),
+                ("q_rows", ctypes.c_int32), ("kv_len", ctypes.c_int32),
+                ("head", ctypes.c_int32), ("item", ctypes.c_int32)]
+
+
+class WorklistHeader(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("abi_version", ctypes.c_uint32),
+                ("total_bytes", ctypes.c_uint64), ("q_rows", ctypes.c_int64),
+                ("kv_rows", ctypes.c_int64), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("block_m", ctypes.c_int32), ("n_items", ctypes.c_int32),
+                ("n_tiles", ctypes.c_int32), ("n_slots", ctypes.c_int32),
+                ("cost_c0", ctypes.c_int32), ("tiles_offset", ctypes.c_uint64),
+                ("slots_offset", ctypes.c_uint64), ("total_cost", ctypes.c_int64),
+                ("max_slot_cost", ctypes.c_int64), ("reserved", ctypes.c_uint64 * 4)]
+
+
+TILE_DTYPE = np.dtype([("q_row0", "<i8"), ("kv_row0", "<i8"), ("q_rows", "<i4"),
+                       ("kv_len", "<i4"), ("head", "<i4"), ("item", "<i4")])
+
+assert ctypes.sizeof(Item) == 32 and ctypes.sizeof(Tile) == 32
+assert ctypes.sizeof(WorklistHeader) == 128 and ctypes.sizeof(Problem) == 32
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m coalesced_attention_amd.build` "
+                          "(there is no fallback path)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, fp = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.zl_abi_version.restype = ctypes.c_int
+    lib.zl_abi_version.argtypes = []
+    lib.zl_status_string.restype = ctypes.c_char_p
+    lib.zl_status_string.argtypes = [ctypes.c_int]
+    lib.zl_last_error.restype = ctypes.c_char_p
+    lib.zl_last_error.argtypes = []
+    lib.zl_build_worklist.restype = ctypes.c_int
+    lib.zl_build_worklist.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Item), i32, i32, vp,
+                                      ctypes.POINTER(ctypes.c_size_t)]
+    lib.zl_coalesced_attn_fwd.restype = ctypes.c_int
+    lib.zl_coalesced_attn_fwd.argtypes = [vp, vp, vp, vp, vp, fp, fp, vp]
+    lib.zl_merge_partials.restype = ctypes.c_int
+    lib.zl_merge_partials.argtypes = [i32, i64, i32, i32, i32, i32, fp, fp, i64, fp, fp, vp]
+    return lib
+
+
+lib = _load()
+ABI_VERSION = lib.zl_abi_version()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != ZL_OK:
+        raise ZlError(rc, where, lib.zl_last_error().decode())
+
+
+def _items_array(items: Iterable) -> ctypes.Array:
+    rows = [it.as_tuple() if hasattr(it, "as_tuple") else tuple(it) for it in items]
+    arr = (Item * max(1, len(rows)))()
+    for i, (q_off, q_len, kv_off, kv_len, h0, hc) in enumerate(rows):
+        arr[i] = Item(q_off, kv_off, q_len, kv_len, h0, hc)
+    return arr, len(rows)
+
+
+class Worklist:
+    """A built worklist: host bytes (numpy) and, once uploaded, a device copy."""
+
+    def __init__(self, host: np.ndarray):
+        self.host = host
+        self.header = WorklistHeader.from_buffer(host)
+        self.device = None
+
+    @property
+    def n_tiles(self) -> int:
+        return self.header.n_tiles
+
+    @property
+    def n_slots(self) -> int:
+        return self.header.n_slots
+
+    def tiles(self) -> np.ndarray:
+        h = self.header
+        off = h.tiles_offset
+        return self.host[off:off + h.n_tiles * 32].view(TILE_DTYPE)
+
+    def slots(self) -> np.ndarray:
+        h = self.header
+        if h.n_slots == 0:
+            return np.zeros(0, np.int32)
+        off = h.slots_offset
+        return self.host[off:off + 4 * (h.n_slots + 1)].view(np.int32)
+
+    def to(self, device) -> "Worklist":
+        import torch
+        self.device = torch.from_numpy(self.host).to(device)
+        return self
+
+    def host_ptr(self) -> int:
+        return self.host.ctypes.data
+
+
+def default_slots(device=None) -> int:
+    """One static slot per compute unit of the device."""
+    import torch
+    return torch.cuda.get_device_properties(device if device is not None else 0).multi_processor_count
+
+
+def build_worklist(items: Iterable, q_rows: int, kv_rows: int, num_heads: int, head_dim: int,
+                   softmax_scale: float = 0.0, n_slots: int = 0, device=None) -> Worklist:
+    """zl_build_worklist. ``items`` are (q_off, q_len, kv_off, kv_len,
+    head_begin, head_cnt) tuples or objects with ``as_tuple()``. With
+    ``device`` the worklist is also copied there."""
+    arr, n = _items_array(items)
+    prob = Problem(q_rows, kv_rows, num_heads, head_dim, softmax_scale, 0)
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.zl_build_worklist(ctypes.byref(prob), arr, n, n_slots, None, ctypes.byref(nbytes)),
+           "zl_build_worklist(size)")
+    host = np.zeros((nbytes.value + 7) // 8, dtype=np.uint64).view(np.uint8)[:nbytes.value]
+    _check(lib.zl_build_worklist(ctypes.byref(prob), arr, n, n_slots, host.ctypes.data,
+                                 ctypes.byref(nbytes)), "zl_build_worklist")
+    wl = Worklist(host)
+    if device is not None:
+        wl.to(device)
+    return wl
+
+
+def _stream_handle(stream, device) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _check_qkv(wl: Worklist, q, k, v):
+    import torch
+    h = wl.header
+    for name, t, rows in (("q", q, h.q_rows), ("k", k, h.kv_rows), ("v", v, h.kv_rows)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+        if tuple(t.shape) != (rows, h.num_heads, h.head_dim):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, worklist expects "
+                             f"{(rows, h.num_heads, h.head_dim)}")
+
+
+def coalesced_attn_fwd(wl: Worklist, q, k, v, o=None, lse=None, stream=None):
+    """zl_coalesced_attn_fwd. Returns (o [q_rows, H, d] fp32, lse [q_rows, H] fp32).
+    Rows no item covers are left as they were in ``o``/``lse``."""
+    import torch
+    _check_qkv(wl, q, k, v)
+    h = wl.header
+    if wl.device is None:
+        wl.to(q.device)
+    if o is None:
+        o = torch.empty((h.q_rows, h.num_heads, h.head_dim), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((h.q_rows, h.num_heads), dtype=torch.float32, device=q.device)
+    if o.dtype != torch.float32 or lse.dtype != torch.float32 or not o.is_contiguous() \
+            or not lse.is_contiguous():
+        raise ValueError("o and lse must be contiguous fp32")
+    if tuple(o.shape) != (h.q_rows, h.num_heads, h.head_dim) or tuple(lse.shape) != (h.q_rows, h.num_heads):
+        raise ValueError("o / lse shape does not match the worklist")
+    _check(lib.zl_coalesced_attn_fwd(wl.host_ptr(), wl.device.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                     v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                     _stream_handle(stream, q.device)), "zl_coalesced_attn_fwd")
+    return o, lse
+
+
+def merge_partials(o, lse, row0: int, n_parts: int, rows: int, part_row_stride: int,
+                   head_begin: int, head_cnt: int, o_out=None, lse_out=None, stream=None):
+    """zl_merge_partials over parts stored in ``o`` [T, H, d] / ``lse`` [T, H]
+    starting at ``row0``. Returns (o_out [rows, H, d], lse_out [rows, H])."""
+    import torch
+    T, H, d = o.shape
+    if o.dtype != torch.float32 or lse.dtype != torch.float32 or not o.is_contiguous() \
+            or not lse.is_contiguous() or tuple(lse.shape) != (T, H):
+        raise ValueError("o [T,H,d] and lse [T,H] must be contiguous fp32")
+    if row0 < 0 or row0 + (n_parts - 1) * part_row_stride + rows > T:
+        raise ValueError("parts exceed the buffers")
+    if o_out is None:
+        o_out = torch.empty((rows, H, d), dtype=torch.float32, device=o.device)
+    if lse_out is None:
+        lse_out = torch.empty((rows, H), dtype=torch.float32, device=o.device)
+    if tuple(o_out.shape) != (rows, H, d) or tuple(lse_out.shape) != (rows, H) \
+            or not o_out.is_contiguous() or not lse_out.is_contiguous():
+        raise ValueError("o_out / lse_out shape mismatch")
+    _check(lib.zl_merge_partials(n_parts, rows, H, head_begin, head_cnt, d,
+                                 o.data_ptr() + row0 * H * d * 4, lse.data_ptr() + row0 * H * 4,
+                                 part_row_stride, o_out.data_ptr(), lse_out.data_ptr(),
+                                 _stream_handle(stream, o.device)), "zl_merge_partials")
+    return o_out, lse_out

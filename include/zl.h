@@ -1,0 +1,175 @@
+/*
+ * zl.h - C ABI of the MI355X (gfx950) coalesced attention library, libzl.so.
+ *
+ * What it computes
+ *   One GPU runs one rank's share of a mixed image/video batch: whole short
+ *   sequences side by side with distributed-attention shards, all in one
+ *   launch (the "coalesced attention engine" of the newx.sg page "Zellige:
+ *   Moldable Sequence Placement for Mixed Image-Video DiT Training",
+ *   Abstract). A shard is one split theta = (q, h, k) of a sequence's
+ *   queries, heads and key/value states (pith.science review of arXiv
+ *   2608.01150, "What carries the argument"); on one GPU it is simply a work
+ *   item with a query row range, a head range and a key/value row range.
+ *   Each item is dense, exact, non-causal softmax attention (same review,
+ *   "Assumptions", paper Sec. II, after FlashAttention [7]).
+ *
+ * Conventions
+ *   - Q is [q_rows, num_heads, head_dim] bf16, K and V are
+ *     [kv_rows, num_heads, head_dim] bf16, row-major and contiguous.
+ *   - O is [q_rows, num_heads, head_dim] fp32 and LSE is [q_rows, num_heads]
+ *     fp32; LSE is the natural log of sum_j exp(scale * q.k_j).
+ *   - The caller owns every buffer, host and device. The library never
+ *     allocates device memory, never synchronises, and launches only on the
+ *     stream it is given (a hipStream_t passed as void*; NULL = the null
+ *     stream). Device pointers must be 16-byte aligned.
+ *   - Every call returns ZL_OK (0) or a negative ZL_ERR_* code; no C++
+ *     exception crosses the ABI. zl_last_error() gives a thread-local text.
+ *   - All argument checks run on the host before any HIP call, so a bad
+ *     argument never reaches a kernel.
+ */
+#ifndef ZL_H_
+#define ZL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZL_ABI_VERSION 1
+#define ZL_WORKLIST_MAGIC 0x31574c5au /* "ZLW1" little-endian */
+
+enum zl_status {
+  ZL_OK = 0,
+  ZL_ERR_NULL = -1,     /* a required pointer is NULL */
+  ZL_ERR_SHAPE = -2,    /* head_dim not 64/128, num_heads < 1, negative sizes */
+  ZL_ERR_RANGE = -3,    /* an item lies outside the rows or heads */
+  ZL_ERR_OVERLAP = -4,  /* two items write the same (query row, head) */
+  ZL_ERR_BUFSIZE = -5,  /* host buffer too small */
+  ZL_ERR_ALIGN = -6,    /* a device pointer is not 16-byte aligned */
+  ZL_ERR_WORKLIST = -7, /* bad magic, version or header in a worklist */
+  ZL_ERR_HIP = -8,      /* a HIP call failed; detail in zl_last_error() */
+  ZL_ERR_ARG = -9       /* any other invalid argument */
+};
+
+/* One work item: query rows [q_off, q_off+q_len) attend to key/value rows
+ * [kv_off, kv_off+kv_len) on heads [head_begin, head_begin+head_cnt).
+ * A whole sequence of length L is (q_len = L, kv_len = L, all heads); a
+ * theta = (q, h, k) shard holds about L/q queries, H/h heads, L/k keys.
+ * q_len = 0 or head_cnt = 0 is a no-op; kv_len = 0 gives O = 0 and
+ * LSE = -inf on the item's rows. 32 bytes. */
+typedef struct zl_item {
+  int64_t q_off;
+  int64_t kv_off;
+  int32_t q_len;
+  int32_t kv_len;
+  int32_t head_begin;
+  int32_t head_cnt;
+} zl_item;
+
+/* Shapes shared by every item of one launch. softmax_scale <= 0 selects
+ * 1/sqrt(head_dim). */
+typedef struct zl_problem {
+  int64_t q_rows;
+  int64_t kv_rows;
+  int32_t num_heads;
+  int32_t head_dim;
+  float softmax_scale;
+  int32_t reserved; /* must be 0 */
+} zl_problem;
+
+/* Worklist buffer = header, then tiles, then slot offsets.
+ * A forward tile is block_m query rows of one item on one head, against the
+ * item's whole key range. Tiles are ordered by the stable LPT rule: cost =
+ * q_rows * kv_len + cost_c0, sorted by cost, largest first, ties kept in
+ * (item, head, query block) order; with n_slots > 0 each tile in that order
+ * goes to the least-loaded slot (lowest index on ties) and the tile array
+ * is stored slot by slot, slot s owning tiles [slots[s], slots[s+1]). With
+ * n_slots == 0 the tile array is the LPT order and the launch has one
+ * workgroup per tile. */
+typedef struct zl_tile {
+  int64_t q_row0;  /* first query row (packed) */
+  int64_t kv_row0; /* first key/value row (packed) */
+  int32_t q_rows;  /* 1..block_m */
+  int32_t kv_len;  /* >= 0 */
+  int32_t head;
+  int32_t item;
+} zl_tile;
+
+typedef struct zl_worklist_header {
+  uint32_t magic;       /* ZL_WORKLIST_MAGIC */
+  uint32_t abi_version; /* ZL_ABI_VERSION */
+  uint64_t total_bytes;
+  int64_t q_rows;
+  int64_t kv_rows;
+  int32_t num_heads;
+  int32_t head_dim;
+  float softmax_scale; /* resolved (> 0) */
+  int32_t block_m;     /* query rows per forward tile */
+  int32_t n_items;
+  int32_t n_tiles;
+  int32_t n_slots;
+  int32_t cost_c0;
+  uint64_t tiles_offset; /* bytes from the start of the buffer */
+  uint64_t slots_offset; /* int32_t[n_slots + 1]; unused when n_slots == 0 */
+  int64_t total_cost;
+  int64_t max_slot_cost; /* makespan of the static schedule (0 if n_slots == 0) */
+  uint64_t reserved[4];
+} zl_worklist_header; /* 128 bytes */
+
+int zl_abi_version(void);
+const char* zl_status_string(int status);
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* zl_last_error(void);
+
+/* Build the tile schedule for one launch on the host. Two calls: with
+ * host_buf == NULL only *bytes is set to the size needed; then, with a
+ * buffer of at least that many bytes (8-byte aligned), the worklist is
+ * written there and *bytes is set to its size. No allocation, no HIP call.
+ * The caller copies the buffer to device memory unchanged; a worklist is
+ * immutable and can serve any number of launches (every layer of a step).
+ * Errors: ZL_ERR_NULL, ZL_ERR_SHAPE, ZL_ERR_RANGE, ZL_ERR_OVERLAP,
+ * ZL_ERR_BUFSIZE, ZL_ERR_ARG (n_items < 0, n_slots < 0 or > 1<<20).
+ * The schedule is the stable LPT reading of "stably schedules and fuses
+ * whole sequences and distributed-attention shards on shared ranks"
+ * (pith.science review of arXiv 2608.01150, "What carries the argument"). */
+int zl_build_worklist(const zl_problem* problem, const zl_item* items, int32_t n_items,
+                      int32_t n_slots, void* host_buf, size_t* bytes);
+
+/* Coalesced forward: for every item, head and query row,
+ *   O = softmax(scale * q K^T) V,  LSE = ln sum_j exp(scale * q.k_j),
+ * non-causal, over the item's own key range (exact attention: pith.science
+ * review, "Assumptions", Sec. II / FlashAttention [7]; whole sequences and
+ * shards in one launch: newx.sg page, Abstract).
+ * h_wl: the worklist in host memory (read for the launch shape); d_wl: the
+ * same bytes in device memory. q, k, v: bf16 device buffers; o, lse: fp32
+ * device buffers. Only (row, head) pairs that some item covers are written.
+ * Asynchronous on `stream`. Errors: ZL_ERR_NULL, ZL_ERR_WORKLIST,
+ * ZL_ERR_ALIGN, ZL_ERR_HIP. */
+int zl_coalesced_attn_fwd(const void* h_wl, const void* d_wl, const void* q, const void* k,
+                          const void* v, float* o, float* lse, void* stream);
+
+/* Merge of KV-split partials. A k-split shard computes attention of the
+ * same queries against disjoint key ranges (pith.science review, "What
+ * carries the argument": theta splits key/value states); the exact result
+ * over the union follows from the parts' LSE: with M = max_p LSE_p,
+ * w_p = exp(LSE_p - M), W = sum_p w_p:  LSE = M + ln W,
+ * O = sum_p (w_p / W) O_p. If every part has LSE = -inf: O = 0, LSE = -inf.
+ * Part p's rows start p * part_row_stride rows after o_parts / lse_parts;
+ * every buffer is laid out [rows, num_heads, head_dim] (O) and
+ * [rows, num_heads] (LSE); only heads [head_begin, head_begin+head_cnt) are
+ * read and written. o_out / lse_out must not overlap the parts.
+ * Errors: ZL_ERR_NULL, ZL_ERR_SHAPE, ZL_ERR_RANGE, ZL_ERR_ARG (n_parts < 1
+ * or > 64, part_row_stride < rows, overlapping output), ZL_ERR_ALIGN,
+ * ZL_ERR_HIP. */
+int zl_merge_partials(int32_t n_parts, int64_t rows, int32_t num_heads, int32_t head_begin,
+                      int32_t head_cnt, int32_t head_dim, const float* o_parts,
+                      const float* lse_parts, int64_t part_row_stride, float* o_out,
+                      float* lse_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZL_H_ */

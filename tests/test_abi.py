@@ -1,0 +1,137 @@
+"""The C-ABI library on the CPU: it loads, exports what include/zl.h declares,
+its worklist equals the reference LPT schedule bit for bit, and every
+argument error is rejected on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from coalesced_attention_amd import workloads as W
+from coalesced_attention_amd import zl
+from oracle.worklist import lpt_schedule
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zl.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zl_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert set(declared) == set(zl.EXPORTS)
+    for name in declared:
+        assert hasattr(zl.lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    text = open(HEADER).read()
+    assert zl.ABI_VERSION == int(re.search(r"#define ZL_ABI_VERSION (\d+)", text).group(1))
+    for code in zl.STATUS:
+        assert zl.lib.zl_status_string(code)
+    assert zl.lib.zl_status_string(-1234) == b"unknown status"
+
+
+@pytest.mark.parametrize("cfg,n_slots", [(0, 0), (0, 3), (1, 256), (2, 0), (2, 256), (2, 97), (3, 256),
+                                         (3, 1)])
+def test_worklist_matches_reference_schedule(cfg, n_slots):
+    wl = W.config(cfg)
+    built = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim,
+                              n_slots=n_slots)
+    h = built.header
+    assert h.magic == zl.WORKLIST_MAGIC and h.abi_version == zl.ABI_VERSION
+    assert (h.q_rows, h.kv_rows, h.num_heads, h.head_dim) == (wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim)
+    assert h.softmax_scale == np.float32(1 / np.sqrt(wl.head_dim))
+    ref, begin, loads = lpt_schedule(wl.items, h.block_m, n_slots, h.cost_c0)
+    got = built.tiles()
+    assert h.n_tiles == len(ref) == len(got)
+    want = np.array([(t.q_row0, t.kv_row0, t.q_rows, t.kv_len, t.head, t.item) for t in ref], dtype=zl.TILE_DTYPE)
+    assert np.array_equal(got, want)
+    if n_slots:
+        assert list(built.slots()) == begin
+        assert h.max_slot_cost == max(loads)
+    assert h.total_cost == sum(t.cost for t in ref)
+
+
+def test_worklist_is_deterministic():
+    wl = W.config(2)
+    a = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, 24, 128, n_slots=256)
+    b = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, 24, 128, n_slots=256)
+    assert np.array_equal(a.host, b.host)
+
+
+def _rc_build(items, q_rows=1000, kv_rows=1000, H=4, d=128, n_slots=0, scale=0.0, reserved=0,
+              buf=True, nbytes=None):
+    arr, n = zl._items_array(items)
+    prob = zl.Problem(q_rows, kv_rows, H, d, scale, reserved)
+    size = ctypes.c_size_t(0)
+    rc = zl.lib.zl_build_worklist(ctypes.byref(prob), arr, n, n_slots, None, ctypes.byref(size))
+    if rc or not buf:
+        return rc
+    host = np.zeros(size.value // 8 + 1, np.uint64)
+    size2 = ctypes.c_size_t(size.value if nbytes is None else nbytes)
+    return zl.lib.zl_build_worklist(ctypes.byref(prob), arr, n, n_slots, host.ctypes.data, ctypes.byref(size2))
+
+
+def test_build_errors():
+    ok = [(0, 10, 0, 10, 0, 4)]
+    assert _rc_build(ok) == 0
+    assert _rc_build(ok, d=96) == -2
+    assert _rc_build(ok, H=0) == -2
+    assert _rc_build([(995, 10, 0, 10, 0, 4)]) == -3           # rows past q_rows
+    assert _rc_build([(0, 10, 995, 10, 0, 4)]) == -3           # keys past kv_rows
+    assert _rc_build([(0, 10, 0, 10, 2, 3)]) == -3             # heads past H
+    assert _rc_build([(0, -1, 0, 10, 0, 4)]) == -3
+    assert _rc_build([(0, 10, 0, 10, 0, 2), (5, 10, 0, 10, 1, 2)]) == -4   # shared (row, head)
+    assert _rc_build([(0, 10, 0, 10, 0, 2), (5, 10, 0, 10, 2, 2)]) == 0    # disjoint heads
+    assert _rc_build([(0, 10, 0, 10, 0, 4), (10, 10, 0, 10, 0, 4)]) == 0   # adjacent rows
+    assert _rc_build(ok, n_slots=-1) == -9
+    assert _rc_build(ok, reserved=1) == -9
+    assert _rc_build(ok, nbytes=64) == -5
+    assert _rc_build(ok, scale=float("inf")) == -9
+    prob = zl.Problem(10, 10, 1, 64, 0.0, 0)
+    size = ctypes.c_size_t(0)
+    assert zl.lib.zl_build_worklist(None, None, 0, 0, None, ctypes.byref(size)) == -1
+    assert zl.lib.zl_build_worklist(ctypes.byref(prob), None, 1, 0, None, ctypes.byref(size)) == -1
+    assert zl.lib.zl_build_worklist(ctypes.byref(prob), None, 0, 0, None, ctypes.byref(size)) == 0
+    assert b"overlap" in zl.lib.zl_status_string(-4)
+
+
+def test_empty_and_zero_length_items():
+    wl = zl.build_worklist([(0, 0, 0, 5, 0, 2), (0, 3, 0, 0, 0, 2), (3, 4, 0, 5, 1, 0)], 10, 10, 2, 64)
+    t = wl.tiles()
+    assert wl.n_tiles == 2 and set(t["kv_len"]) == {0} and set(t["q_rows"]) == {3}
+
+
+def test_fwd_and_merge_reject_bad_arguments_before_any_hip_call():
+    wl = W.config(0)
+    built = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim)
+    p = 1 << 20  # aligned fake device address; never dereferenced on these paths
+    f = zl.lib.zl_coalesced_attn_fwd
+    assert f(None, p, p, p, p, p, p, None) == -1
+    assert f(built.host_ptr(), None, p, p, p, p, p, None) == -1
+    assert f(built.host_ptr(), p, p + 8, p, p, p, p, None) == -6
+    bad = built.host.copy()
+    bad[:4] = 0
+    assert f(bad.ctypes.data, p, p, p, p, p, p, None) == -7
+    bad = built.host.copy()
+    bad.view(np.uint32)[1] = 99  # abi version
+    assert f(bad.ctypes.data, p, p, p, p, p, p, None) == -7
+    bad = built.host.copy()
+    zl.WorklistHeader.from_buffer(bad).total_bytes = 64
+    assert f(bad.ctypes.data, p, p, p, p, p, p, None) == -7
+    m = zl.lib.zl_merge_partials
+    assert m(2, 10, 4, 0, 4, 128, None, p, 10, p, p, None) == -1
+    assert m(2, 10, 4, 0, 4, 96, p, p, 10, p, p, None) == -2
+    assert m(2, 10, 4, 2, 3, 128, p, p, 10, p, p, None) == -3
+    assert m(0, 10, 4, 0, 4, 128, p, p, 10, p, p, None) == -9
+    assert m(2, 10, 4, 0, 4, 128, p, p, 5, p, p, None) == -9   # stride < rows
+    assert m(2, 10, 4, 0, 4, 128, p + 4, p, 10, p, p, None) == -6
+    q = 1 << 30
+    assert m(2, 10, 4, 0, 4, 128, p, q, 10, p, q + (1 << 24), None) == -9   # output overlaps parts

@@ -1,0 +1,240 @@
+"""GPU parity of the coalesced forward and the partial merge against the fp64
+oracle, through the C ABI, plus GPU-side invariants and edge cases."""
+
+import math
+
+import numpy as np
+import pytest
+
+from coalesced_attention_amd import workloads as W
+from oracle import attention as orc
+
+from gpu_util import LSE_MAX_ABS, Stats, log, oracle_compare, run_fwd, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from coalesced_attention_amd import zl  # noqa: F401  (fails loudly if libzl.so is missing)
+
+
+_CACHE = {}
+
+
+def _workload(c):
+    if c not in _CACHE:
+        _CACHE.clear()
+        wl = W.config(c)
+        log(f"drawing inputs of config {c} ({wl.name})")
+        inp = W.make_inputs(wl)
+        _CACHE[c] = (wl, inp, to_device(inp))
+    return _CACHE[c]
+
+
+def _host(x):
+    return x.float().numpy()
+
+
+# ----------------------------------------------------------------- configs
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("c", [0, 1, 2, 3])
+def test_forward_parity(c):
+    wl, inp, (q, k, v) = _workload(c)
+    log(f"config {c}: forward on GPU, {len(wl.items)} items")
+    built, o, lse = run_fwd(wl.items, q, k, v, wl.num_heads, wl.head_dim)
+    O, LSE = o.cpu().numpy(), lse.cpu().numpy()
+    log(f"config {c}: {built.n_tiles} tiles done; oracle check")
+    st = oracle_compare(Stats(), wl.items, _host(inp.q), _host(inp.k), _host(inp.v), O, LSE,
+                        wl.softmax_scale, seed=c)
+    st.assert_gates(f"config {c} forward")
+    # every covered (row, head) written, nothing else
+    cov = np.zeros((wl.q_rows, wl.num_heads), bool)
+    for it in wl.items:
+        cov[it.q_off:it.q_off + it.q_len, it.head_begin:it.head_begin + it.head_cnt] = True
+    assert np.array_equal(~np.isnan(LSE), cov)
+    assert np.array_equal(~np.isnan(O).any(-1), cov)
+    assert np.array_equal(np.isnan(O).all(-1), ~cov)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("c", [0, 3])
+def test_merge_parity(c):
+    from coalesced_attention_amd import zl
+    wl, inp, (q, k, v) = _workload(c)
+    built, o, lse = run_fwd(wl.items, q, k, v, wl.num_heads, wl.head_dim)
+    m = wl.merges[0]
+    mo, ml = zl.merge_partials(o, lse, m.row0, m.n_parts, m.rows, m.part_row_stride,
+                               m.head_begin, m.head_cnt)
+    torch.cuda.synchronize()
+    MO, ML = mo.cpu().numpy(), ml.cpu().numpy()
+    # the merged queries are the partials' shared query rows, against all keys
+    whole = W.Item(m.row0, m.rows, m.ref_kv_off, m.ref_kv_len, m.head_begin, m.head_cnt)
+    st = Stats()
+    rows = W.sample_rows(whole, seed=7, full_limit=1024)
+    if c == 3:
+        rows = rows[::4]  # full-range oracle rows cost 220k keys each
+    Qh, Kh, Vh = _host(inp.q), _host(inp.k), _host(inp.v)
+    for h in range(m.head_begin, m.head_begin + m.head_cnt):
+        o_ref, l_ref = orc.coalesced_forward_rows(Qh, Kh, Vh, whole, h, rows, wl.softmax_scale)
+        st.add(h, MO[rows, h], o_ref, ML[rows, h], l_ref)
+    st.assert_gates(f"config {c} merge")
+    if m.ref_q_off >= 0:  # the same queries also ran as one whole item on the GPU
+        O, LSE = o.cpu().numpy(), lse.cpu().numpy()
+        ref = slice(m.ref_q_off, m.ref_q_off + m.rows)
+        hs = slice(m.head_begin, m.head_begin + m.head_cnt)
+        assert np.abs(MO[:, hs] - O[ref, hs]).max() < 2e-2
+        assert np.abs(ML[:, hs] - LSE[ref, hs]).max() < LSE_MAX_ABS
+
+
+def test_merge_kernel_against_oracle_merge():
+    from coalesced_attention_amd import zl
+    rng = np.random.default_rng(3)
+    for d, n_parts, rows, H, h0, hc in [(128, 2, 300, 5, 1, 3), (64, 3, 77, 2, 0, 2), (128, 5, 16, 24, 4, 12)]:
+        stride = rows + 9
+        T = (n_parts - 1) * stride + rows + 4
+        o = rng.standard_normal((T, H, d)).astype(np.float32)
+        lse = (3 * rng.standard_normal((T, H))).astype(np.float32)
+        lse[rng.random((T, H)) < 0.1] = -np.inf  # empty parts
+        lse[4 + 5, :] = -np.inf
+        lse[4 + stride + 5, :] = -np.inf  # row 5: every part empty when n_parts == 2
+        if n_parts > 2:
+            for p in range(2, n_parts):
+                lse[4 + p * stride + 5, :] = -np.inf
+        to = torch.from_numpy(o).cuda()
+        tl = torch.from_numpy(lse).cuda()
+        mo, ml = zl.merge_partials(to, tl, 4, n_parts, rows, stride, h0, hc)
+        torch.cuda.synchronize()
+        parts_o = np.stack([o[4 + p * stride:4 + p * stride + rows, h0:h0 + hc] for p in range(n_parts)])
+        parts_l = np.stack([lse[4 + p * stride:4 + p * stride + rows, h0:h0 + hc] for p in range(n_parts)])
+        ro, rl = orc.merge_partials(parts_o, parts_l)
+        go, gl = mo.cpu().numpy()[:, h0:h0 + hc], ml.cpu().numpy()[:, h0:h0 + hc]
+        np.testing.assert_allclose(go, ro, rtol=1e-5, atol=1e-5)
+        assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
+        fin = np.isfinite(rl)
+        np.testing.assert_allclose(gl[fin], rl[fin], rtol=1e-6, atol=1e-5)
+        assert np.all(go[5] == 0) and np.all(np.isneginf(gl[5]))
+
+
+# ----------------------------------------------------------------- invariants
+
+def test_bitwise_determinism_and_schedule_independence():
+    wl = W.config(2)
+    # a reduced mixed batch keeps this quick: the shard and 6 images
+    items = wl.items[:1] + wl.items[1:4] + wl.items[25:28]
+    inp = W.make_inputs(wl)
+    q, k, v = to_device(inp)
+    outs = []
+    for n_slots in (256, 256, 0, 97, 1):
+        _, o, lse = run_fwd(items, q, k, v, wl.num_heads, wl.head_dim, n_slots=n_slots)
+        outs.append((o.cpu().numpy(), lse.cpu().numpy()))
+    for o2, l2 in outs[1:]:
+        assert np.array_equal(o2, outs[0][0], equal_nan=True)
+        assert np.array_equal(l2, outs[0][1], equal_nan=True)
+
+
+def test_independence_across_packed_sequences():
+    wl, inp, (q, k, v) = _workload(1)
+    _, o1, l1 = run_fwd(wl.items, q, k, v, wl.num_heads, wl.head_dim)
+    a = wl.items[5]
+    k2, v2, q2 = k.clone(), v.clone(), q.clone()
+    k2[a.kv_off:a.kv_off + a.kv_len] *= -2
+    v2[a.kv_off:a.kv_off + a.kv_len] += 1
+    q2[a.q_off:a.q_off + a.q_len] = 0
+    _, o2, l2 = run_fwd(wl.items, q2, k2, v2, wl.num_heads, wl.head_dim)
+    O1, O2, L1, L2 = (x.cpu().numpy() for x in (o1, o2, l1, l2))
+    mask = np.ones(wl.q_rows, bool)
+    mask[a.q_off:a.q_off + a.q_len] = False
+    assert np.array_equal(O1[mask], O2[mask]) and np.array_equal(L1[mask], L2[mask])
+    assert not np.allclose(O1[~mask], O2[~mask])
+
+
+def test_closed_forms_on_gpu():
+    H, d = 3, 128
+    kv = 1000
+    rng = np.random.default_rng(1)
+    K = torch.from_numpy(rng.standard_normal((kv, H, d)).astype(np.float32)).to(torch.bfloat16).cuda()
+    V = torch.from_numpy(rng.standard_normal((kv, H, d)).astype(np.float32)).to(torch.bfloat16).cuda()
+    Q = torch.zeros((300, H, d), dtype=torch.bfloat16, device="cuda")
+    items = [(0, 300, 0, kv, 0, H)]
+    _, o, lse = run_fwd(items, Q, K, V, H, d)
+    mean_v = V.float().mean(0)
+    assert torch.allclose(o, mean_v.expand_as(o), atol=1e-5, rtol=0)
+    assert torch.allclose(lse, torch.full_like(lse, math.log(kv)), atol=1e-5, rtol=0)
+    Q = torch.from_numpy(rng.standard_normal((300, H, d)).astype(np.float32)).to(torch.bfloat16).cuda()
+    Vc = torch.full_like(V, -1.5)
+    _, o, _ = run_fwd(items, Q, K, Vc, H, d)
+    assert torch.allclose(o, torch.full_like(o, -1.5), atol=2e-3, rtol=0)
+    # one key: O = v, LSE = scale * q.k
+    _, o, lse = run_fwd([(0, 300, 7, 1, 0, H)], Q, K, V, H, d)
+    assert torch.allclose(o, V[7].float().expand_as(o), atol=1e-5, rtol=1e-6)
+    z = (Q.float() * K[7].float()).sum(-1) / math.sqrt(d)
+    assert torch.allclose(lse, z, atol=1e-4, rtol=0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_ragged_edges_and_head_splits(d):
+    H = 4
+    rng = np.random.default_rng(d)
+    cases = [(1, 1), (1, 64), (255, 65), (256, 63), (257, 129), (300, 127), (31, 1000), (513, 256),
+             (5, 0), (0, 10), (40, 2047)]
+    items, q_off, kv_off = [], 0, 0
+    for ql, kl in cases:
+        items.append(W.Item(q_off, ql, kv_off, kl, 0, H))
+        q_off += ql
+        kv_off += kl
+    # a head-split pair sharing query rows (Ulysses-style), different key ranges
+    items.append(W.Item(q_off, 200, 0, 300, 0, 2))
+    items.append(W.Item(q_off, 200, 300, 150, 2, 2))
+    q_off += 200
+    Q = rng.standard_normal((q_off, H, d)).astype(np.float32)
+    K = rng.standard_normal((kv_off, H, d)).astype(np.float32)
+    V = rng.standard_normal((kv_off, H, d)).astype(np.float32)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16) for x in (Q, K, V))
+    for n_slots in (0, 7):
+        _, o, lse = run_fwd(items, q.cuda(), k.cuda(), v.cuda(), H, d, n_slots=n_slots)
+        O, L = o.cpu().numpy(), lse.cpu().numpy()
+        st = Stats()
+        for idx, it in enumerate(items):
+            if it.q_len == 0:
+                continue
+            for h in range(it.head_begin, it.head_begin + it.head_cnt):
+                rows = np.arange(it.q_len)
+                o_ref, l_ref = orc.coalesced_forward_rows(q.float().numpy(), k.float().numpy(),
+                                                          v.float().numpy(), it, h, rows, 1 / math.sqrt(d))
+                if it.kv_len == 0:
+                    assert np.all(O[it.q_off:it.q_off + it.q_len, h] == 0)
+                    assert np.all(np.isneginf(L[it.q_off:it.q_off + it.q_len, h]))
+                    continue
+                st.add(idx, O[it.q_off + rows, h], o_ref, L[it.q_off + rows, h], l_ref)
+        st.assert_gates(f"ragged d={d} n_slots={n_slots}")
+
+
+def test_peaky_queries_exercise_the_running_max():
+    wl = W.config(0)
+    inp = W.make_inputs(wl, q_scale=4.0)
+    q, k, v = to_device(inp)
+    _, o, lse = run_fwd(wl.items, q, k, v, wl.num_heads, wl.head_dim)
+    st = oracle_compare(Stats(), wl.items, _host(inp.q), _host(inp.k), _host(inp.v),
+                        o.cpu().numpy(), lse.cpu().numpy(), wl.softmax_scale)
+    st.assert_gates("config 0, queries x4")
+
+
+def test_key_permutation_within_an_item():
+    wl, inp, (q, k, v) = _workload(1)
+    items = wl.items[:3]
+    _, o1, l1 = run_fwd(items, q, k, v, wl.num_heads, wl.head_dim)
+    a = items[1]
+    perm = torch.randperm(a.kv_len, generator=torch.Generator().manual_seed(0)).cuda() + a.kv_off
+    k2, v2 = k.clone(), v.clone()
+    k2[a.kv_off:a.kv_off + a.kv_len] = k[perm]
+    v2[a.kv_off:a.kv_off + a.kv_len] = v[perm]
+    _, o2, l2 = run_fwd(items, q, k2, v2, wl.num_heads, wl.head_dim)
+    sl = slice(a.q_off, a.q_off + a.q_len)
+    assert (o1[sl] - o2[sl]).abs().max().item() < 2e-3
+    assert (l1[sl] - l2[sl]).abs().max().item() < 1e-4
