@@ -1,0 +1,183 @@
+#!/usr/bin/env python3
+"""Benchmark of the coalesced attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one coalesced forward launch over the mixed rank share: one
+theta = (4, 1, 1) shard of a 32760-token video (8190 queries against all
+32760 keys) packed with 24 whole 1024-token and 32 whole 256-token images,
+24 heads, head_dim 128, bf16 inputs already resident in HBM. The worklist is
+built once per batch on the host (timed separately) and reused, as every
+layer of a training step reuses it. Prints one JSON line.
+
+The KV-split merge (two 27450-row partials on 12 heads) is timed beside it
+and reported in GB/s. The cpu_baseline leg times the fp64 oracle on a
+bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "mixed-batch coalesced attention fwd TFLOP/s and % of bf16 MFMA peak"
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload index (2 = mixed rank share)")
+    ap.add_argument("--n-slots", type=int, default=-1, help="static slots (-1: one per CU, 0: one WG per tile)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-merge", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time")
+    return ap.parse_args()
+
+
+def _events_ms(fn, steps, stream):
+    """Average duration of fn() over `steps` launches, from HIP events
+    recorded on the stream the kernels run on."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(steps):
+            fn()
+        end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def _cpu_baseline(wl, inp, target_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload."""
+    from oracle.attention import coalesced_forward_rows
+    from coalesced_attention_amd.workloads import sample_rows
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    Qh, Kh, Vh = (x.float().numpy() for x in (inp.q, inp.k, inp.v))
+    s = wl.softmax_scale
+    d = wl.head_dim
+    # round-robin over (item, head) units: sampled rows of long items, all
+    # rows of short ones; stop once the target time is spent
+    units = []
+    for idx, it in enumerate(wl.items):
+        rows = sample_rows(it, seed=idx)
+        for h in range(it.head_begin, it.head_begin + it.head_cnt):
+            units.append((it, h, rows))
+    order = np.random.default_rng(0).permutation(len(units))
+    flops = 0
+    rows_done = 0
+    t0 = time.perf_counter()
+    for u in order:
+        it, h, rows = units[u]
+        coalesced_forward_rows(Qh, Kh, Vh, it, h, rows, s)
+        flops += 4 * len(rows) * it.kv_len * d
+        rows_done += len(rows)
+        if time.perf_counter() - t0 > target_s:
+            break
+    el = time.perf_counter() - t0
+    total_rows = sum(it.q_len * it.head_cnt for it in wl.items)
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows_done} of {total_rows} (query row, head) pairs of the same workload "
+                      f"({flops / 1e9:.1f} GFLOP in {el:.1f} s, fp64 numpy)"}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (the multi-GPU "
+              "exchanges are design-only)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from coalesced_attention_amd import workloads as W
+    from coalesced_attention_amd import zl
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    wl = W.config(a.config)
+    inp = W.make_inputs(wl)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    n_slots = zl.default_slots(0) if a.n_slots < 0 else a.n_slots
+
+    t0 = time.perf_counter()
+    built = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim,
+                              n_slots=n_slots)
+    wl_ms = (time.perf_counter() - t0) * 1e3
+    built.to(dev)
+    o = torch.empty((wl.q_rows, wl.num_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((wl.q_rows, wl.num_heads), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        zl.coalesced_attn_fwd(built, q, k, v, o, lse, stream=stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    kern_ms = _events_ms(step, a.steps, stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / a.steps
+
+    flops = wl.flops_fwd()
+    tflops = flops / (ms * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "items": len(wl.items), "q_rows": wl.q_rows,
+                   "kv_rows": wl.kv_rows, "heads": wl.num_heads, "head_dim": wl.head_dim,
+                   "tiles": built.n_tiles, "n_slots": n_slots, "flops_per_step": flops},
+        "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "fwd_kernel<128>", "kernel_ms": round(kern_ms, 4)},
+        "worklist_build_ms": round(wl_ms, 3),
+    }
+
+    if not a.no_merge:
+        # KV-split merge at its full size: 2 partials x 27450 rows x 12 of 24 heads
+        rows, H, d, parts = 27450, 24, 128, 2
+        g = torch.Generator(device=dev).manual_seed(3)
+        po = torch.randn((parts * rows, H, d), generator=g, device=dev)
+        pl = 10 + torch.randn((parts * rows, H), generator=g, device=dev)
+        mo = torch.empty((rows, H, d), device=dev)
+        ml = torch.empty((rows, H), device=dev)
+
+        def merge():
+            zl.merge_partials(po, pl, 0, parts, rows, rows, 0, 12, mo, ml, stream=stream)
+
+        for _ in range(3):
+            merge()
+        torch.cuda.synchronize()
+        mms = _events_ms(merge, 20, stream)
+        mbytes = (parts + 1) * rows * 12 * (d + 1) * 4
+        out["merge"] = {"workload": "kv-split merge, 2 x 27450 rows x 12 heads x 128", "ms": round(mms, 4),
+                        "GB/s": round(mbytes / (mms * 1e-3) / 1e9, 1),
+                        "frac_of_hbm_peak": round(mbytes / (mms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                        "bytes": mbytes}
+
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline(wl, inp, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

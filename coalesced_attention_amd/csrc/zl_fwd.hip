@@ -40,6 +40,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -239,17 +240,12 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const char ZL_LDS* vp = vb + (b * 32 + 16 * u + tr_row) * C::kVP + db * 64 + tr_col;
-          i16x4 lo = lds_read_tr16(vp);
-          i16x4 hi = lds_read_tr16(vp + 8 * C::kVP);
-          bf16x8 a;
-          a[0] = __builtin_bit_cast(__bf16, lo[0]);
-          a[1] = __builtin_bit_cast(__bf16, lo[1]);
-          a[2] = __builtin_bit_cast(__bf16, lo[2]);
-          a[3] = __builtin_bit_cast(__bf16, lo[3]);
-          a[4] = __builtin_bit_cast(__bf16, hi[0]);
-          a[5] = __builtin_bit_cast(__bf16, hi[1]);
-          a[6] = __builtin_bit_cast(__bf16, hi[2]);
-          a[7] = __builtin_bit_cast(__bf16, hi[3]);
+          const i16x4 lo = lds_read_tr16(vp);
+          const i16x4 hi = lds_read_tr16(vp + 8 * C::kVP);
+          // whole-vector concatenation: per-element inserts of bf16 lanes
+          // were lowered to a lossy permute by the compiler
+          const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, cat);
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[b][u], oacc[db], 0, 0, 0);
         }
 

@@ -72,6 +72,11 @@ assert ctypes.sizeof(WorklistHeader) == 128 and ctypes.sizeof(Problem) == 32
 
 
 def _load() -> ctypes.CDLL:
+    # One HIP runtime per process: torch ships its own libamdhip64.so.7 and
+    # loading torch first makes libzl.so's dependency on that soname resolve
+    # to the copy torch already uses (a second runtime in the same process
+    # does not see the GPU, and its streams would not be torch's).
+    import torch  # noqa: F401
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is not built; run `python -m coalesced_attention_amd.build` "
                           "(there is no fallback path)")
