@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "zl.h"
 #include "zl_internal.h"
@@ -51,13 +52,20 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+// Buffer resource word 3 for raw (untyped) dword loads on gfx9-family parts.
+constexpr int kBufferFlags = 0x00020000;
 
 template <int D>
 struct Fwd {
   static constexpr int kWaves = zl::kFwdWaves;
+  static constexpr int kQB = zl::kFwdQueryBlocks;  // 32-query MFMA blocks per wave
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kBlockM = zl::kFwdBlockM;
-  static constexpr int kBN = 64;              // keys per block
+  static constexpr int kBN = zl::kFwdBlockN;  // keys per block
   static constexpr int kKB = kBN / 32;        // 32-key MFMA blocks per key block
   static constexpr int kDS = D / 16;          // 16-wide steps over head_dim
   static constexpr int kDB = D / 32;          // 32-wide output blocks over head_dim
@@ -65,12 +73,13 @@ struct Fwd {
   static constexpr int kVP = D * 2 + 64;      // V row pitch (bytes): 4-row transpose reads hit distinct banks
   static constexpr int kKBytes = kBN * kKP;
   static constexpr int kVBytes = kBN * kVP;
-  static constexpr int kStage = kKBytes + kVBytes;
-  static constexpr int kLdsBytes = 2 * kStage;
+  static constexpr int kLdsBytes = 2 * (kKBytes + kVBytes);
   static constexpr int kChunksPerRow = D / 8;  // 16-byte chunks per row
   static constexpr int kChunks = kBN * kChunksPerRow;
-  static constexpr int kCPT = kChunks / kThreads;  // chunks per thread per tensor
-  static_assert(kChunks % kThreads == 0, "tile load must divide evenly");
+  // chunks per thread per tensor (the last round may leave threads idle)
+  static constexpr int kCPT = (kChunks + kThreads - 1) / kThreads;
+  static_assert(kChunks % kThreads == 0 || kCPT == 1, "partial rounds only when one round");
+  static_assert(kBlockM == kWaves * 32 * kQB, "tile rows");
 };
 
 __device__ __forceinline__ float swap_halves_max(float x) {
@@ -94,6 +103,26 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const char ZL_LDS* p) {
       reinterpret_cast<i16x4 ZL_LDS*>(const_cast<char ZL_LDS*>(p)));
 }
 
+// The tile record is the same for every lane; readfirstlane tells the
+// compiler so, which keeps the derived addresses and the buffer resources in
+// scalar registers.
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ zl_tile uniform_tile(const zl_tile& t) {
+  zl_tile u;
+  u.q_row0 = uniform_i64(t.q_row0);
+  u.kv_row0 = uniform_i64(t.kv_row0);
+  u.q_rows = __builtin_amdgcn_readfirstlane(t.q_rows);
+  u.kv_len = __builtin_amdgcn_readfirstlane(t.kv_len);
+  u.head = __builtin_amdgcn_readfirstlane(t.head);
+  u.item = __builtin_amdgcn_readfirstlane(t.item);
+  return u;
+}
+
 template <int D>
 __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __restrict__ Q,
                                          const __bf16* __restrict__ K,
@@ -101,6 +130,7 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
                                          float* __restrict__ LSE, int H, float c,
                                          char ZL_LDS* smem) {
   using C = Fwd<D>;
+  constexpr int QB = C::kQB, KB = C::kKB, DS = C::kDS, DB = C::kDB, CPT = C::kCPT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -108,16 +138,20 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
   const int half = lane >> 5;
   const int64_t rs = int64_t(H) * D;  // elements between consecutive rows
 
-  // ---- Q^T fragments: query row `qr`, head_dim [ds*16 + 8*half, +8)
-  const int qr = wave * 32 + l32;
-  const bool qvalid = qr < tile.q_rows;
-  bf16x8 qf[C::kDS];
-  {
-    const __bf16* qp = Q + (tile.q_row0 + (qvalid ? qr : 0)) * rs + int64_t(tile.head) * D + 8 * half;
+  // ---- Q^T fragments: query rows wave*32*QB + 32*qb + l32,
+  // head_dim [ds*16 + 8*half, +8)
+  bf16x8 qf[QB][DS];
+  bool qvalid[QB];
 #pragma unroll
-    for (int ds = 0; ds < C::kDS; ++ds) {
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qr = (wave * QB + qb) * 32 + l32;
+    qvalid[qb] = qr < tile.q_rows;
+    const __bf16* qp =
+        Q + (tile.q_row0 + (qvalid[qb] ? qr : 0)) * rs + int64_t(tile.head) * D + 8 * half;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
       bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + ds * 16);
-      qf[ds] = qvalid ? x : bf16x8{};
+      qf[qb][ds] = qvalid[qb] ? x : bf16x8{};
     }
   }
 
@@ -126,119 +160,95 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
   const __bf16* kbase = K + tile.kv_row0 * rs + int64_t(tile.head) * D;
   const __bf16* vbase = V + tile.kv_row0 * rs + int64_t(tile.head) * D;
 
-  u32x4 kreg[C::kCPT], vreg[C::kCPT];
-  auto gload = [&](int blk) {
-#pragma unroll
-    for (int i = 0; i < C::kCPT; ++i) {
-      const int ch = tid + i * C::kThreads;
-      const int row = ch / C::kChunksPerRow, col = ch % C::kChunksPerRow;
-      const int key = blk * C::kBN + row;
-      if (key < kv_len) {
-        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + int64_t(key) * rs + col * 8);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + int64_t(key) * rs + col * 8);
-      } else {
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int stage) {
-    char ZL_LDS* kb = smem + stage * C::kStage;
-    char ZL_LDS* vb = kb + C::kKBytes;
-#pragma unroll
-    for (int i = 0; i < C::kCPT; ++i) {
-      const int ch = tid + i * C::kThreads;
-      const int row = ch / C::kChunksPerRow, col = ch % C::kChunksPerRow;
-      *reinterpret_cast<u32x4 ZL_LDS*>(kb + row * C::kKP + col * 16) = kreg[i];
-      *reinterpret_cast<u32x4 ZL_LDS*>(vb + row * C::kVP + col * 16) = vreg[i];
-    }
-  };
+  // LDS: K stages 0,1 then V stages 0,1.
+  char ZL_LDS* const kst[2] = {smem, smem + C::kKBytes};
+  char ZL_LDS* const vst[2] = {smem + 2 * C::kKBytes, smem + 2 * C::kKBytes + C::kVBytes};
 
-  f32x16 oacc[C::kDB];
+  // Global -> register -> LDS staging with raw buffer loads. The buffer of
+  // block `blk` starts at its first key row and ends at the item's last key,
+  // so rows past kv_len read as zero without a branch. Thread `tid` always
+  // moves the same 16-byte chunks (row, column) of a 64-key tile.
+  int ld_off[CPT];
+  int st_k[CPT], st_v[CPT];
 #pragma unroll
-  for (int i = 0; i < C::kDB; ++i) oacc[i] = f32x16{};
-  float m_use = -INFINITY;  // running max in use, in exp2 units (score * c)
-  float l_part = 0.f;       // this lane's partial row sum (its half of the keys)
-
-  if (nblk > 0) {
-    gload(0);
-    lstore(0);
+  for (int i = 0; i < CPT; ++i) {
+    // threads past the tile's chunk count re-load and re-store chunk 0 of
+    // their row 0 copy: the same bytes the owning thread writes
+    const int ch = (tid + i * C::kThreads) % C::kChunks;
+    const int row = ch / C::kChunksPerRow, col = ch % C::kChunksPerRow;
+    ld_off[i] = int(row * rs + col * 8) * 2;  // < 64 rows of one tile
+    st_k[i] = row * C::kKP + col * 16;
+    st_v[i] = row * C::kVP + col * 16;
   }
-  __syncthreads();
+  u32x4 kreg[CPT], vreg[CPT];
+  auto gload = [&](const __bf16* base, u32x4 (&reg)[CPT], int blk) __attribute__((always_inline)) {
+    // wave-uniform by construction; readfirstlane keeps the descriptor in
+    // scalar registers (a vector descriptor would need a waterfall loop)
+    const int rows = __builtin_amdgcn_readfirstlane(min(C::kBN, max(0, kv_len - blk * C::kBN)));
+    const int64_t addr = uniform_i64(reinterpret_cast<int64_t>(base + int64_t(blk) * C::kBN * rs));
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<__bf16*>(addr), 0,
+                                                        rows * int(rs) * 2, kBufferFlags);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, ld_off[i], 0, 0));
+  };
+  auto lstore = [&](char ZL_LDS* dst, const u32x4 (&reg)[CPT], const int (&off)[CPT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) *reinterpret_cast<u32x4 ZL_LDS*>(dst + off[i]) = reg[i];
+  };
 
-  // Per-lane byte offsets inside a stage.
+  // Per-lane LDS byte offsets.
   const int k_off = l32 * C::kKP + half * 16;
   const int tr_row = 4 * half + ((lane & 15) >> 2);
   const int tr_col = (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
 
-  for (int j = 0; j < nblk; ++j) {
-    if (j + 1 < nblk) gload(j + 1);
-    const char ZL_LDS* kb = smem + (j & 1) * C::kStage;
-    const char ZL_LDS* vb = kb + C::kKBytes;
-
-    // ---- S^T = K Q^T for 64 keys x 32 queries
-    f32x16 s[C::kKB];
+  // S^T = K Q^T for one 64-key block; each K fragment feeds every query block.
+  auto qk = [&](const char ZL_LDS* kb, f32x16 (&s)[QB][KB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int b = 0; b < C::kKB; ++b) {
-      s[b] = f32x16{};
+    for (int b = 0; b < KB; ++b) {
 #pragma unroll
-      for (int ds = 0; ds < C::kDS; ++ds) {
-        bf16x8 a = lds_read_b128(kb + b * 32 * C::kKP + k_off + ds * 32);
-        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], s[b], 0, 0, 0);
+      for (int qb = 0; qb < QB; ++qb) s[qb][b] = f32x16{};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const bf16x8 a = lds_read_b128(kb + b * 32 * C::kKP + k_off + ds * 32);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ds], s[qb][b], 0, 0, 0);
       }
     }
-
-    // ---- mask keys past the item's end (last block only)
-    if ((j + 1) * C::kBN > kv_len) {
+  };
+  // Keys at or past kv_len (only in the last block) get -inf.
+  auto mask = [&](f32x16 (&s)[QB][KB], int blk) __attribute__((always_inline)) {
 #pragma unroll
-      for (int b = 0; b < C::kKB; ++b)
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int b = 0; b < KB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j * C::kBN + b * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= kv_len) s[b][r] = -INFINITY;
+          const int key = blk * C::kBN + b * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key >= kv_len) s[qb][b][r] = -INFINITY;
         }
-    }
-
-    // ---- row max over the block, both halves
-    float mx = s[0][0];
+  };
+  // Row max over both halves of the block, in exp2 units.
+  auto rowmax = [&](const f32x16 (&s)[KB]) __attribute__((always_inline)) {
+    float m0 = fmaxf(s[0][0], s[0][1]), m1 = fmaxf(s[0][2], s[0][3]);
 #pragma unroll
-    for (int b = 0; b < C::kKB; ++b)
+    for (int b = 0; b < KB; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-    mx = swap_halves_max(mx) * c;
-
-    // ---- raise the max in use only when it grew by more than the slack
-    if (mx > m_use + kRescaleSlack) {
-      const float alpha = __builtin_amdgcn_exp2f(m_use - mx);
-      m_use = mx;
-      l_part *= alpha;
-#pragma unroll
-      for (int i = 0; i < C::kDB; ++i) oacc[i] *= alpha;
-    }
-
-    // ---- P = exp2(S c - m), partial row sums, bf16 B operands
-    bf16x8 pf[C::kKB][2];
-    float lsum = 0.f;
-#pragma unroll
-    for (int b = 0; b < C::kKB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -m_use));
-        lsum += p;
-        pf[b][r >> 3][r & 7] = (__bf16)p;
+      for (int r = (b == 0 ? 4 : 0); r < 16; r += 4) {
+        m0 = fmaxf(m0, fmaxf(s[b][r], s[b][r + 1]));
+        m1 = fmaxf(m1, fmaxf(s[b][r + 2], s[b][r + 3]));
       }
-    l_part += lsum;
-
-    // ---- O^T += V^T P^T
-    // k-slot e of the B operand (b, u) in half `half` holds key
-    // b*32 + 16u + 8(e/4) + 4*half + e%4: the lane's own registers 8u..8u+7.
-    // The A operand reads the same keys of V transposed, 4 keys per read.
+    return swap_halves_max(fmaxf(m0, m1)) * c;
+  };
+  // O^T += V^T P^T for one 64-key block; each V^T fragment feeds every query block.
+  auto pv = [&](const char ZL_LDS* vb, const bf16x8 (&pf)[QB][KB][2], f32x16 (&o)[QB][DB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db)
+    for (int b = 0; b < KB; ++b)
 #pragma unroll
-      for (int b = 0; b < C::kKB; ++b)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int db = 0; db < DB; ++db) {
           const char ZL_LDS* vp = vb + (b * 32 + 16 * u + tr_row) * C::kVP + db * 64 + tr_col;
           const i16x4 lo = lds_read_tr16(vp);
           const i16x4 hi = lds_read_tr16(vp + 8 * C::kVP);
@@ -246,28 +256,182 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
           // were lowered to a lossy permute by the compiler
           const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           const bf16x8 a = __builtin_bit_cast(bf16x8, cat);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[b][u], oacc[db], 0, 0, 0);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][b][u], o[qb][db], 0, 0, 0);
         }
+  };
 
-    if (j + 1 < nblk) lstore((j + 1) & 1);
+  f32x16 oacc[QB][DB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[qb][i] = f32x16{};
+  float m_use[QB], l_part[QB];  // max in use (exp2 units) and this lane's partial row sum
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_use[qb] = -INFINITY;
+    l_part[qb] = 0.f;
+  }
+  f32x16 s_a[QB][KB], s_b[QB][KB];
+
+  // ---- prologue: K(0), V(0), K(1) to LDS; S(0) and its max
+  if (nblk > 0) {
+    gload(kbase, kreg, 0);
+    gload(vbase, vreg, 0);
+    lstore(kst[0], kreg, st_k);
+    lstore(vst[0], vreg, st_v);
+    gload(kbase, kreg, 1);
+    lstore(kst[1], kreg, st_k);
+  }
+  __syncthreads();
+  if (nblk > 0) {
+    qk(kst[0], s_a);
+    if (nblk == 1) mask(s_a, 0);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_use[qb] = rowmax(s_a[qb]);
+  }
+  __syncthreads();  // K stage 0 is refilled by the first iteration
+
+  // ---- one 64-key block. Iteration j turns S(j) (in `sc`) into P(j) in
+  // place and accumulates O += V(j)^T P(j)^T, while computing S(j+1) into
+  // `sn`. The work is issued as short windows in program order, each a
+  // vector-ALU chunk followed by the matrix-core chunk it does not depend
+  // on, so the MFMAs of one window run under the vector work of the next:
+  //   phase A, 4 windows: exponentials of 16 scores of S(j) | 8 MFMAs of S(j+1)
+  //   phase B, 4 windows: bf16 pack + row sums of 16 probabilities and part
+  //                       of the max of S(j+1) | 8 MFMAs of O += V^T P^T
+  // K runs two blocks ahead of V so each LDS stage is rewritten only after
+  // the barrier that ends its last reader.
+  // The last iteration also runs the S(j+1) MFMAs, on a K stage holding
+  // zeros (the loads past the last block return zero); its result is unused.
+  const bool ragged = (kv_len % C::kBN) != 0;
+  auto iteration = [&](int j, f32x16 (&sc)[QB][KB], f32x16 (&sn)[QB][KB])
+      __attribute__((always_inline)) {
+    const bool has_next = j + 1 < nblk;
+    constexpr int kWin = 2 * KB;              // windows per phase
+    constexpr int kPer = QB * KB * 16 / kWin;  // scores per phase-A window
+    gload(kbase, kreg, j + 2);  // all zero past the last block
+    gload(vbase, vreg, j + 1);
+    // Keys past kv_len exist only in the last block; mask them just before
+    // they are exponentiated. (The max of S(j+1) taken in phase B may see
+    // the zero scores of the zero-filled rows: that only raises the max in
+    // use, which the normalisation cancels.)
+    if (ragged && j + 1 == nblk) mask(sc, j);
+    const char ZL_LDS* kb = kst[(j + 1) & 1];
+    // phase A
+#pragma unroll
+    for (int w = 0; w < kWin; ++w) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const int idx = w * kPer + e;
+        const int qb = idx / (KB * 16), b = (idx / 16) % KB, r = idx % 16;
+        sc[qb][b][r] = __builtin_amdgcn_exp2f(fmaf(sc[qb][b][r], c, -m_use[qb]));
+      }
+      {
+        const int b = w / 2, ds0 = (w % 2) * (DS / 2);
+#pragma unroll
+        for (int ds = ds0; ds < ds0 + DS / 2; ++ds) {
+          const bf16x8 a = lds_read_b128(kb + b * 32 * C::kKP + k_off + ds * 32);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            sn[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                a, qf[qb][ds], ds == 0 ? f32x16{} : sn[qb][b], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // phase B
+    const char ZL_LDS* vb = vst[j & 1];
+    float mx0[QB], mx1[QB];
+#pragma unroll
+    for (int w = 0; w < kWin; ++w) {
+      const int b = w / 2, u = w % 2;
+      bf16x8 pf[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pe = sc[qb][b][8 * u + e];
+          ls += pe;
+          pf[qb][e] = (__bf16)pe;
+        }
+        l_part[qb] += ls;
+        {
+          // max over the 8 scores of S(j+1) at the same positions
+          const f32x16& t = sn[qb][b];
+          const float m4 = fmaxf(fmaxf(t[8 * u], t[8 * u + 1]), fmaxf(t[8 * u + 2], t[8 * u + 3]));
+          const float m8 = fmaxf(fmaxf(t[8 * u + 4], t[8 * u + 5]), fmaxf(t[8 * u + 6], t[8 * u + 7]));
+          if (w == 0) {
+            mx0[qb] = m4;
+            mx1[qb] = m8;
+          } else {
+            mx0[qb] = fmaxf(mx0[qb], m4);
+            mx1[qb] = fmaxf(mx1[qb], m8);
+          }
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const char ZL_LDS* vp = vb + (b * 32 + 16 * u + tr_row) * C::kVP + db * 64 + tr_col;
+        const i16x4 lo = lds_read_tr16(vp);
+        const i16x4 hi = lds_read_tr16(vp + 8 * C::kVP);
+        // whole-vector concatenation: per-element inserts of bf16 lanes
+        // were lowered to a lossy permute by the compiler
+        const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, cat);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb], oacc[qb][db], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lstore(kst[j & 1], kreg, st_k);
+    lstore(vst[(j + 1) & 1], vreg, st_v);
     __syncthreads();
+    if (has_next) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float mx = swap_halves_max(fmaxf(mx0[qb], mx1[qb])) * c;
+        // Raise the max in use only when a row grew past the slack. The
+        // branch is taken by the whole wave or not at all, so the O
+        // accumulators are only touched when some row needs it.
+        const bool grow = mx > m_use[qb] + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m_use[qb] - mx) : 1.f;
+          m_use[qb] = grow ? mx : m_use[qb];
+          l_part[qb] *= alpha;
+#pragma unroll
+          for (int i = 0; i < DB; ++i) oacc[qb][i] *= alpha;
+        }
+      }
+    }
+  };
+  for (int j = 0; j < nblk; j += 2) {
+    iteration(j, s_a, s_b);
+    if (j + 1 < nblk) iteration(j + 1, s_b, s_a);
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l)
-  const float l_tot = swap_halves_sum(l_part);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse = l_tot > 0.f ? kLn2 * (m_use + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
-  if (qvalid) {
-    float* op = O + (tile.q_row0 + qr) * rs + int64_t(tile.head) * D + 4 * half;
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = swap_halves_sum(l_part[qb]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse = l_tot > 0.f ? kLn2 * (m_use[qb] + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
+    if (qvalid[qb]) {
+      const int qr = (wave * QB + qb) * 32 + l32;
+      float* op = O + (tile.q_row0 + qr) * rs + int64_t(tile.head) * D + 4 * half;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 x = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
-                   oacc[db][4 * g + 3] * inv};
-        *reinterpret_cast<f32x4*>(op + db * 32 + 8 * g) = x;
-      }
-    if (half == 0) LSE[(tile.q_row0 + qr) * H + tile.head] = lse;
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& a = oacc[qb][db];
+          f32x4 x = {a[4 * g] * inv, a[4 * g + 1] * inv, a[4 * g + 2] * inv, a[4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(op + db * 32 + 8 * g) = x;
+        }
+      if (half == 0) LSE[(tile.q_row0 + qr) * H + tile.head] = lse;
+    }
   }
 }
 
@@ -286,8 +450,10 @@ __global__ __launch_bounds__(Fwd<D>::kThreads, 1) void fwd_kernel(
     t0 = blockIdx.x;
     t1 = t0 + 1;
   }
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  t1 = __builtin_amdgcn_readfirstlane(t1);
   for (int t = t0; t < t1; ++t) {
-    const zl_tile tile = tiles[t];
+    const zl_tile tile = uniform_tile(tiles[t]);
     run_tile<D>(tile, Q, K, V, O, LSE, H, c, smem);
     __syncthreads();  // LDS is reused by the next tile
   }

@@ -9,9 +9,23 @@
 
 namespace zl {
 
-// Forward tile: 8 waves x 32 query rows (one 32-row MFMA block per wave).
-constexpr int kFwdWaves = 8;
-constexpr int kFwdBlockM = kFwdWaves * 32;
+// Forward tile: kFwdWaves waves x kFwdQueryBlocks blocks of 32 query rows,
+// streaming kFwdBlockN keys per step. The defaults can be overridden at
+// build time (-DZL_FWD_WAVES=...) to compare shapes.
+#ifndef ZL_FWD_WAVES
+#define ZL_FWD_WAVES 8
+#endif
+#ifndef ZL_FWD_QUERY_BLOCKS
+#define ZL_FWD_QUERY_BLOCKS 1
+#endif
+#ifndef ZL_FWD_BLOCK_N
+#define ZL_FWD_BLOCK_N 64
+#endif
+constexpr int kFwdWaves = ZL_FWD_WAVES;
+constexpr int kFwdQueryBlocks = ZL_FWD_QUERY_BLOCKS;
+constexpr int kFwdBlockM = kFwdWaves * 32 * kFwdQueryBlocks;
+constexpr int kFwdBlockN = ZL_FWD_BLOCK_N;
+static_assert(kFwdBlockM == 256, "the worklist cuts 256-row tiles");
 // Per-tile fixed cost in (query row x key) units used by the LPT rule: the
 // prologue and epilogue of a tile cost about as much as 64 keys of work.
 constexpr int kCostC0PerRow = 64;
