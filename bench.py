@@ -40,7 +40,38 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (scale reference for FETCH/WRITE_SIZE)")
     return ap.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash(files):
+    """sha256 over the sources a profiled kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter runs
+    (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads for a
+    plain copy of known size), or None when the record is missing or the
+    kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC) as fh:
+            rec = json.load(fh)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash(rec["sources"]):
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
 
 
 def _events_ms(fn, steps, stream):
@@ -109,6 +140,15 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if a.calibrate_copy:
+        n = 1 << 28  # 1 GiB of fp32
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4}), flush=True)
+        return
     wl = W.config(a.config)
     inp = W.make_inputs(wl)
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
@@ -148,7 +188,8 @@ def main():
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "fwd_kernel<128>", "kernel_ms": round(kern_ms, 4)},
+                     "traffic": measured_traffic("fwd_kernel<128>"), "kernel": "fwd_kernel<128>",
+                     "kernel_ms": round(kern_ms, 4)},
         "worklist_build_ms": round(wl_ms, 3),
     }
 
@@ -172,7 +213,7 @@ def main():
         out["merge"] = {"workload": "kv-split merge, 2 x 27450 rows x 12 heads x 128", "ms": round(mms, 4),
                         "GB/s": round(mbytes / (mms * 1e-3) / 1e9, 1),
                         "frac_of_hbm_peak": round(mbytes / (mms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                        "bytes": mbytes}
+                        "bytes": mbytes, "traffic": measured_traffic("merge_kernel<128>")}
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(wl, inp, a.cpu_seconds)

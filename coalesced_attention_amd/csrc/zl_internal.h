@@ -9,21 +9,17 @@
 
 namespace zl {
 
-// Forward tile: kFwdWaves waves x kFwdQueryBlocks blocks of 32 query rows,
-// streaming kFwdBlockN keys per step. The defaults can be overridden at
-// build time (-DZL_FWD_WAVES=...) to compare shapes.
+// Forward tile: kFwdWaves waves x 32 query rows, streaming kFwdBlockN keys
+// per step. The key block can be overridden at build time
+// (-DZL_FWD_BLOCK_N=32) to compare shapes.
 #ifndef ZL_FWD_WAVES
 #define ZL_FWD_WAVES 8
-#endif
-#ifndef ZL_FWD_QUERY_BLOCKS
-#define ZL_FWD_QUERY_BLOCKS 1
 #endif
 #ifndef ZL_FWD_BLOCK_N
 #define ZL_FWD_BLOCK_N 64
 #endif
 constexpr int kFwdWaves = ZL_FWD_WAVES;
-constexpr int kFwdQueryBlocks = ZL_FWD_QUERY_BLOCKS;
-constexpr int kFwdBlockM = kFwdWaves * 32 * kFwdQueryBlocks;
+constexpr int kFwdBlockM = kFwdWaves * 32;
 constexpr int kFwdBlockN = ZL_FWD_BLOCK_N;
 static_assert(kFwdBlockM == 256, "the worklist cuts 256-row tiles");
 // Per-tile fixed cost in (query row x key) units used by the LPT rule: the
