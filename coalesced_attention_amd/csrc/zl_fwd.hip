@@ -52,6 +52,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr int kXcds = 8;               // accelerator complex dies of an MI355X
 // s_waitcnt immediate with lgkmcnt and expcnt at their maximum and vmcnt 0:
 // adding n waits until at most n vector-memory operations are outstanding.
 constexpr int kWaitLoads = 0x0F70;
@@ -396,8 +397,14 @@ __global__ __launch_bounds__(Fwd<D>::kThreads, 1) void fwd_kernel(
   char ZL_LDS* smem = (char ZL_LDS*)(smem_raw);  // generic -> LDS address space
   int t0, t1;
   if (n_slots > 0) {
-    t0 = slots[blockIdx.x];
-    t1 = slots[blockIdx.x + 1];
+    // Workgroups are dispatched round-robin over the XCDs (w -> XCD w % 8),
+    // each with its own L2. Consecutive slots receive consecutive tiles of
+    // the LPT order, i.e. the query blocks of one (item, head) that read the
+    // same K/V, so slot s runs on a workgroup of XCD s / (n_slots / 8).
+    const int w = blockIdx.x;
+    const int s = n_slots % kXcds == 0 ? (w % kXcds) * (n_slots / kXcds) + w / kXcds : w;
+    t0 = slots[s];
+    t1 = slots[s + 1];
   } else {
     t0 = blockIdx.x;
     t1 = t0 + 1;

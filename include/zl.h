@@ -87,7 +87,10 @@ typedef struct zl_problem {
  * goes to the least-loaded slot (lowest index on ties) and the tile array
  * is stored slot by slot, slot s owning tiles [slots[s], slots[s+1]). With
  * n_slots == 0 the tile array is the LPT order and the launch has one
- * workgroup per tile. */
+ * workgroup per tile. When n_slots is a multiple of 8, slot s runs on
+ * workgroup w with s = (w % 8) * (n_slots / 8) + w / 8: workgroups are
+ * dispatched round-robin over the 8 XCDs, so consecutive slots (the query
+ * blocks of one item and head, which read the same K/V) share an L2. */
 typedef struct zl_tile {
   int64_t q_row0;  /* first query row (packed) */
   int64_t kv_row0; /* first key/value row (packed) */
@@ -126,7 +129,8 @@ const char* zl_last_error(void);
 /* Build the tile schedule for one launch on the host. Two calls: with
  * host_buf == NULL only *bytes is set to the size needed; then, with a
  * buffer of at least that many bytes (8-byte aligned), the worklist is
- * written there and *bytes is set to its size. No allocation, no HIP call.
+ * written there and *bytes is set to its size. Host memory only (temporary
+ * vectors); no device allocation and no HIP call.
  * The caller copies the buffer to device memory unchanged; a worklist is
  * immutable and can serve any number of launches (every layer of a step).
  * Errors: ZL_ERR_NULL, ZL_ERR_SHAPE, ZL_ERR_RANGE, ZL_ERR_OVERLAP,
