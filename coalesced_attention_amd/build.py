@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libzl.so")
 
-SOURCES = ["zl_host.cpp", "zl_fwd.hip", "zl_merge.hip"]
+SOURCES = ["zl_host.cpp", "zl_fwd.hip", "zl_merge.hip", "zl_bwd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -26,6 +26,8 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # inputs carry no NaNs: lets fmaxf map to v_max3 without canonicalizing
     "-fno-honor-nans",
+    # fp32 atomicAdd on device memory as the hardware atomic (no CAS loop)
+    "-munsafe-fp-atomics",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -51,13 +51,22 @@ int check_worklist(const void* h_wl, const zl_worklist_header** hdr) {
       h->n_slots < 0 || h->n_slots > kMaxSlots || h->block_m != kFwdBlockM ||
       !(h->softmax_scale > 0.f) || h->q_rows < 0 || h->kv_rows < 0)
     return fail(ZL_ERR_WORKLIST, "worklist header fields out of range");
+  if (h->block_n_bwd != kBwdBlockN || h->n_bwd_tiles < 0)
+    return fail(ZL_ERR_WORKLIST, "worklist backward fields out of range");
   uint64_t need = h->tiles_offset + uint64_t(h->n_tiles) * sizeof(zl_tile);
   if (h->n_slots > 0) {
     if (h->slots_offset < need) return fail(ZL_ERR_WORKLIST, "worklist slot table overlaps tiles");
     need = h->slots_offset + uint64_t(h->n_slots + 1) * sizeof(int32_t);
   }
+  if (h->bwd_tiles_offset < need) return fail(ZL_ERR_WORKLIST, "worklist sections overlap");
+  need = h->bwd_tiles_offset + uint64_t(h->n_bwd_tiles) * sizeof(zl_tile);
+  if (h->n_slots > 0) {
+    if (h->bwd_slots_offset < need) return fail(ZL_ERR_WORKLIST, "worklist sections overlap");
+    need = h->bwd_slots_offset + uint64_t(h->n_slots + 1) * sizeof(int32_t);
+  }
   if (h->tiles_offset < sizeof(zl_worklist_header) || (h->tiles_offset & 15u) ||
-      (h->slots_offset & 15u) || need > h->total_bytes)
+      (h->slots_offset & 15u) || (h->bwd_tiles_offset & 15u) || (h->bwd_slots_offset & 15u) ||
+      need > h->total_bytes)
     return fail(ZL_ERR_WORKLIST, "worklist offsets inconsistent with its size");
   *hdr = h;
   return ZL_OK;
@@ -127,6 +136,61 @@ struct TileKey {
   int64_t cost;
 };
 
+// Stable LPT: order by cost, largest first, equal costs in cut order (item,
+// head, first row) -- a total order, so std::sort gives the stable result.
+// With n_slots == 0 the order itself is written; otherwise each tile goes to
+// the least-loaded slot (lowest index on ties) and the tiles are written slot
+// by slot with offsets [n_slots + 1].
+int schedule(std::vector<TileKey>& tiles, int32_t n_slots, zl_tile* out, int32_t* slots,
+             int64_t* total_cost, int64_t* makespan) {
+  std::sort(tiles.begin(), tiles.end(), [](const TileKey& a, const TileKey& b) {
+    if (a.cost != b.cost) return a.cost > b.cost;
+    if (a.t.item != b.t.item) return a.t.item < b.t.item;
+    if (a.t.head != b.t.head) return a.t.head < b.t.head;
+    if (a.t.q_row0 != b.t.q_row0) return a.t.q_row0 < b.t.q_row0;
+    return a.t.kv_row0 < b.t.kv_row0;
+  });
+  const int32_t n = int32_t(tiles.size());
+  *total_cost = 0;
+  *makespan = 0;
+  for (const TileKey& k : tiles) *total_cost += k.cost;
+  if (n_slots == 0) {
+    for (int32_t t = 0; t < n; ++t) out[t] = tiles[size_t(t)].t;
+    return ZL_OK;
+  }
+  try {
+    // Least-loaded slot, lowest index on ties: a binary heap ordered by
+    // (load, slot); then a stable counting sort lays the tiles out by slot.
+    std::vector<std::pair<int64_t, int32_t>> heap;
+    std::vector<int32_t> slot_of(static_cast<size_t>(n));
+    std::vector<int32_t> count(static_cast<size_t>(n_slots) + 1, 0);
+    std::vector<int64_t> load(static_cast<size_t>(n_slots), 0);
+    heap.reserve(size_t(n_slots));
+    for (int32_t s = 0; s < n_slots; ++s) heap.emplace_back(0, s);
+    auto cmp = [](const std::pair<int64_t, int32_t>& a, const std::pair<int64_t, int32_t>& b) {
+      return a > b;  // min-heap on (load, slot)
+    };
+    std::make_heap(heap.begin(), heap.end(), cmp);
+    for (int32_t t = 0; t < n; ++t) {
+      std::pop_heap(heap.begin(), heap.end(), cmp);
+      const int32_t s = heap.back().second;
+      heap.back().first += tiles[size_t(t)].cost;
+      slot_of[size_t(t)] = s;
+      load[size_t(s)] = heap.back().first;
+      ++count[size_t(s) + 1];
+      std::push_heap(heap.begin(), heap.end(), cmp);
+    }
+    for (int32_t s = 0; s < n_slots; ++s) count[size_t(s) + 1] += count[size_t(s)];
+    for (int32_t s = 0; s <= n_slots; ++s) slots[s] = count[size_t(s)];
+    std::vector<int32_t> fill(count.begin(), count.end() - 1);
+    for (int32_t t = 0; t < n; ++t) out[fill[size_t(slot_of[size_t(t)])]++] = tiles[size_t(t)].t;
+    for (int64_t l : load) *makespan = std::max(*makespan, l);
+  } catch (const std::bad_alloc&) {
+    return fail(ZL_ERR_ARG, "out of host memory scheduling %d tiles", n);
+  }
+  return ZL_OK;
+}
+
 }  // namespace
 
 extern "C" int zl_build_worklist(const zl_problem* problem, const zl_item* items, int32_t n_items,
@@ -152,11 +216,20 @@ extern "C" int zl_build_worklist(const zl_problem* problem, const zl_item* items
     const zl_item& it = items[i];
     n_tiles64 += int64_t(it.head_cnt) * ((int64_t(it.q_len) + block_m - 1) / block_m);
   }
-  if (n_tiles64 > INT32_MAX) return fail(ZL_ERR_ARG, "too many tiles");
-  const int32_t n_tiles = int32_t(n_tiles64);
+  int64_t n_bwd64 = 0;
+  for (int32_t i = 0; i < n_items; ++i) {
+    const zl_item& it = items[i];
+    if (it.q_len > 0)
+      n_bwd64 += int64_t(it.head_cnt) * ((int64_t(it.kv_len) + kBwdBlockN - 1) / kBwdBlockN);
+  }
+  if (n_tiles64 > INT32_MAX || n_bwd64 > INT32_MAX) return fail(ZL_ERR_ARG, "too many tiles");
+  const int32_t n_tiles = int32_t(n_tiles64), n_bwd_tiles = int32_t(n_bwd64);
+  const uint64_t slot_bytes = n_slots > 0 ? uint64_t(n_slots + 1) * 4 : 0;
   const uint64_t tiles_off = align_up(sizeof(zl_worklist_header), 256);
   const uint64_t slots_off = align_up(tiles_off + uint64_t(n_tiles) * sizeof(zl_tile), 256);
-  const uint64_t total = align_up(slots_off + (n_slots > 0 ? uint64_t(n_slots + 1) * 4 : 0), 256);
+  const uint64_t bwd_tiles_off = align_up(slots_off + slot_bytes, 256);
+  const uint64_t bwd_slots_off = align_up(bwd_tiles_off + uint64_t(n_bwd_tiles) * sizeof(zl_tile), 256);
+  const uint64_t total = align_up(bwd_slots_off + slot_bytes, 256);
   if (!host_buf) {
     *bytes = size_t(total);
     return ZL_OK;
@@ -164,72 +237,54 @@ extern "C" int zl_build_worklist(const zl_problem* problem, const zl_item* items
   if (*bytes < total) return fail(ZL_ERR_BUFSIZE, "worklist needs %llu bytes", (unsigned long long)total);
   if (reinterpret_cast<uintptr_t>(host_buf) & 7u) return fail(ZL_ERR_ALIGN, "host_buf must be 8-byte aligned");
 
+  char* base = static_cast<char*>(host_buf);
+  std::memset(base, 0, size_t(total));
+  auto* hdr = reinterpret_cast<zl_worklist_header*>(base);
+
+  // Forward tiles: block_m query rows x one head x the item's key range.
   const int64_t c0 = int64_t(block_m) * kCostC0PerRow;
   std::vector<TileKey> tiles;
   try {
     tiles.reserve(size_t(n_tiles));
+    for (int32_t i = 0; i < n_items; ++i) {
+      const zl_item& it = items[i];
+      for (int32_t h = it.head_begin; h < it.head_begin + it.head_cnt; ++h)
+        for (int32_t r0 = 0; r0 < it.q_len; r0 += block_m) {
+          const int32_t rows = std::min(block_m, it.q_len - r0);
+          tiles.push_back(TileKey{zl_tile{it.q_off + r0, it.kv_off, rows, it.kv_len, h, i},
+                                  int64_t(rows) * it.kv_len + c0});
+        }
+    }
   } catch (const std::bad_alloc&) {
     return fail(ZL_ERR_ARG, "out of host memory for %d tiles", n_tiles);
   }
-  for (int32_t i = 0; i < n_items; ++i) {
-    const zl_item& it = items[i];
-    for (int32_t h = it.head_begin; h < it.head_begin + it.head_cnt; ++h)
-      for (int32_t r0 = 0; r0 < it.q_len; r0 += block_m) {
-        const int32_t rows = std::min(block_m, it.q_len - r0);
-        TileKey k;
-        k.t = zl_tile{it.q_off + r0, it.kv_off, rows, it.kv_len, h, i};
-        k.cost = int64_t(rows) * it.kv_len + c0;
-        tiles.push_back(k);
-      }
-  }
-  // Largest cost first; equal costs keep cut order (item, head, query row),
-  // which is a total order, so std::sort gives the stable result.
-  std::sort(tiles.begin(), tiles.end(), [](const TileKey& a, const TileKey& b) {
-    if (a.cost != b.cost) return a.cost > b.cost;
-    if (a.t.item != b.t.item) return a.t.item < b.t.item;
-    if (a.t.head != b.t.head) return a.t.head < b.t.head;
-    return a.t.q_row0 < b.t.q_row0;
-  });
-
-  char* base = static_cast<char*>(host_buf);
-  std::memset(base, 0, size_t(total));
-  auto* hdr = reinterpret_cast<zl_worklist_header*>(base);
-  auto* out = reinterpret_cast<zl_tile*>(base + tiles_off);
   int64_t total_cost = 0, makespan = 0;
-  for (const TileKey& k : tiles) total_cost += k.cost;
+  rc = schedule(tiles, n_slots, reinterpret_cast<zl_tile*>(base + tiles_off),
+                reinterpret_cast<int32_t*>(base + slots_off), &total_cost, &makespan);
+  if (rc) return rc;
 
-  if (n_slots == 0) {
-    for (int32_t t = 0; t < n_tiles; ++t) out[t] = tiles[size_t(t)].t;
-  } else {
-    // Least-loaded slot, lowest index on ties: a binary heap ordered by
-    // (load, slot). The chosen slot of each tile is kept in LPT order and
-    // the tiles are then laid out slot by slot (a stable counting sort).
-    std::vector<std::pair<int64_t, int32_t>> heap;
-    std::vector<int32_t> slot_of(static_cast<size_t>(n_tiles));
-    std::vector<int32_t> count(static_cast<size_t>(n_slots) + 1, 0);
-    std::vector<int64_t> load(size_t(n_slots), 0);
-    heap.reserve(size_t(n_slots));
-    for (int32_t s = 0; s < n_slots; ++s) heap.emplace_back(0, s);
-    auto cmp = [](const std::pair<int64_t, int32_t>& a, const std::pair<int64_t, int32_t>& b) {
-      return a > b;  // min-heap on (load, slot)
-    };
-    std::make_heap(heap.begin(), heap.end(), cmp);
-    for (int32_t t = 0; t < n_tiles; ++t) {
-      std::pop_heap(heap.begin(), heap.end(), cmp);
-      const int32_t s = heap.back().second;
-      heap.back().first += tiles[size_t(t)].cost;
-      slot_of[size_t(t)] = s;
-      load[size_t(s)] = heap.back().first;
-      ++count[size_t(s) + 1];
-      std::push_heap(heap.begin(), heap.end(), cmp);
+  // Backward tiles: block_n_bwd keys x one head x all of the item's queries.
+  const int64_t c0_bwd = int64_t(kBwdBlockN) * kCostC0PerRow;
+  std::vector<TileKey> btiles;
+  try {
+    btiles.reserve(size_t(n_bwd_tiles));
+    for (int32_t i = 0; i < n_items; ++i) {
+      const zl_item& it = items[i];
+      if (it.q_len == 0) continue;
+      for (int32_t h = it.head_begin; h < it.head_begin + it.head_cnt; ++h)
+        for (int32_t k0 = 0; k0 < it.kv_len; k0 += kBwdBlockN) {
+          const int32_t keys = std::min(kBwdBlockN, it.kv_len - k0);
+          btiles.push_back(TileKey{zl_tile{it.q_off, it.kv_off + k0, it.q_len, keys, h, i},
+                                   int64_t(keys) * it.q_len + c0_bwd});
+        }
     }
-    for (int32_t s = 0; s < n_slots; ++s) count[size_t(s) + 1] += count[size_t(s)];
-    auto* slots = reinterpret_cast<int32_t*>(base + slots_off);
-    for (int32_t s = 0; s <= n_slots; ++s) slots[s] = count[size_t(s)];
-    std::vector<int32_t> fill(count.begin(), count.end() - 1);
-    for (int32_t t = 0; t < n_tiles; ++t) out[fill[size_t(slot_of[size_t(t)])]++] = tiles[size_t(t)].t;
-    for (int64_t l : load) makespan = std::max(makespan, l);
+  } catch (const std::bad_alloc&) {
+    return fail(ZL_ERR_ARG, "out of host memory for %d backward tiles", n_bwd_tiles);
   }
+  int64_t bwd_total = 0, bwd_makespan = 0;
+  rc = schedule(btiles, n_slots, reinterpret_cast<zl_tile*>(base + bwd_tiles_off),
+                reinterpret_cast<int32_t*>(base + bwd_slots_off), &bwd_total, &bwd_makespan);
+  if (rc) return rc;
 
   hdr->magic = ZL_WORKLIST_MAGIC;
   hdr->abi_version = ZL_ABI_VERSION;
@@ -249,6 +304,11 @@ extern "C" int zl_build_worklist(const zl_problem* problem, const zl_item* items
   hdr->slots_offset = n_slots > 0 ? slots_off : 0;
   hdr->total_cost = total_cost;
   hdr->max_slot_cost = makespan;
+  hdr->block_n_bwd = kBwdBlockN;
+  hdr->n_bwd_tiles = n_bwd_tiles;
+  hdr->bwd_tiles_offset = bwd_tiles_off;
+  hdr->bwd_slots_offset = n_slots > 0 ? bwd_slots_off : 0;
+  hdr->bwd_max_slot_cost = bwd_makespan;
   *bytes = size_t(total);
   return ZL_OK;
 }

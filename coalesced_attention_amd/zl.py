@@ -25,7 +25,7 @@ WORKLIST_MAGIC = 0x31574C5A
 
 # Symbols include/zl.h declares (checked by the CPU tests).
 EXPORTS = ("zl_abi_version", "zl_status_string", "zl_last_error", "zl_build_worklist",
-           "zl_coalesced_attn_fwd", "zl_merge_partials")
+           "zl_coalesced_attn_fwd", "zl_merge_partials", "zl_coalesced_attn_bwd")
 
 
 class ZlError(RuntimeError):
@@ -61,7 +61,9 @@ class WorklistHeader(ctypes.Structure):
                 ("n_tiles", ctypes.c_int32), ("n_slots", ctypes.c_int32),
                 ("cost_c0", ctypes.c_int32), ("tiles_offset", ctypes.c_uint64),
                 ("slots_offset", ctypes.c_uint64), ("total_cost", ctypes.c_int64),
-                ("max_slot_cost", ctypes.c_int64), ("reserved", ctypes.c_uint64 * 4)]
+                ("max_slot_cost", ctypes.c_int64), ("block_n_bwd", ctypes.c_int32),
+                ("n_bwd_tiles", ctypes.c_int32), ("bwd_tiles_offset", ctypes.c_uint64),
+                ("bwd_slots_offset", ctypes.c_uint64), ("bwd_max_slot_cost", ctypes.c_int64)]
 
 
 TILE_DTYPE = np.dtype([("q_row0", "<i8"), ("kv_row0", "<i8"), ("q_rows", "<i4"),
@@ -95,6 +97,8 @@ def _load() -> ctypes.CDLL:
     lib.zl_coalesced_attn_fwd.argtypes = [vp, vp, vp, vp, vp, fp, fp, vp]
     lib.zl_merge_partials.restype = ctypes.c_int
     lib.zl_merge_partials.argtypes = [i32, i64, i32, i32, i32, i32, fp, fp, i64, fp, fp, vp]
+    lib.zl_coalesced_attn_bwd.restype = ctypes.c_int
+    lib.zl_coalesced_attn_bwd.argtypes = [vp, vp, vp, vp, vp, fp, fp, vp, fp, fp, fp, fp, vp]
     return lib
 
 
@@ -141,6 +145,18 @@ class Worklist:
         if h.n_slots == 0:
             return np.zeros(0, np.int32)
         off = h.slots_offset
+        return self.host[off:off + 4 * (h.n_slots + 1)].view(np.int32)
+
+    def bwd_tiles(self) -> np.ndarray:
+        h = self.header
+        off = h.bwd_tiles_offset
+        return self.host[off:off + h.n_bwd_tiles * 32].view(TILE_DTYPE)
+
+    def bwd_slots(self) -> np.ndarray:
+        h = self.header
+        if h.n_slots == 0:
+            return np.zeros(0, np.int32)
+        off = h.bwd_slots_offset
         return self.host[off:off + 4 * (h.n_slots + 1)].view(np.int32)
 
     def to(self, device) -> "Worklist":
@@ -216,6 +232,37 @@ def coalesced_attn_fwd(wl: Worklist, q, k, v, o=None, lse=None, stream=None):
                                      v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                      _stream_handle(stream, q.device)), "zl_coalesced_attn_fwd")
     return o, lse
+
+
+def coalesced_attn_bwd(wl: Worklist, q, k, v, o, lse, dout, dq=None, dk=None, dv=None, ws=None,
+                       stream=None):
+    """zl_coalesced_attn_bwd. Gradients ACCUMULATE into dq/dk/dv (fresh zero
+    tensors when not given). Returns (dq, dk, dv)."""
+    import torch
+    _check_qkv(wl, q, k, v)
+    h = wl.header
+    if wl.device is None:
+        wl.to(q.device)
+    if dout.dtype != torch.bfloat16 or not dout.is_contiguous() or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("dout must be a contiguous bf16 tensor shaped like q")
+    if o.dtype != torch.float32 or tuple(o.shape) != tuple(q.shape) or not o.is_contiguous():
+        raise ValueError("o must be the forward's fp32 output")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (h.q_rows, h.num_heads) or not lse.is_contiguous():
+        raise ValueError("lse must be the forward's fp32 [q_rows, H] output")
+    z = lambda shape: torch.zeros(shape, dtype=torch.float32, device=q.device)
+    dq = z(q.shape) if dq is None else dq
+    dk = z(k.shape) if dk is None else dk
+    dv = z(v.shape) if dv is None else dv
+    ws = torch.empty((h.q_rows, h.num_heads), dtype=torch.float32, device=q.device) if ws is None else ws
+    for name, t, shape in (("dq", dq, q.shape), ("dk", dk, k.shape), ("dv", dv, v.shape),
+                           ("ws", ws, (h.q_rows, h.num_heads))):
+        if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous fp32 of shape {tuple(shape)}")
+    _check(lib.zl_coalesced_attn_bwd(wl.host_ptr(), wl.device.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                     v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                                     _stream_handle(stream, q.device)), "zl_coalesced_attn_bwd")
+    return dq, dk, dv
 
 
 def merge_partials(o, lse, row0: int, n_parts: int, rows: int, part_row_stride: int,

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define ZL_ABI_VERSION 1
+#define ZL_ABI_VERSION 2
 #define ZL_WORKLIST_MAGIC 0x31574c5au /* "ZLW1" little-endian */
 
 enum zl_status {
@@ -118,7 +118,16 @@ typedef struct zl_worklist_header {
   uint64_t slots_offset; /* int32_t[n_slots + 1]; unused when n_slots == 0 */
   int64_t total_cost;
   int64_t max_slot_cost; /* makespan of the static schedule (0 if n_slots == 0) */
-  uint64_t reserved[4];
+  /* Backward tiles: block_n_bwd keys of one item on one head, against all of
+   * the item's query rows; same LPT rule (cost = q_rows * kv_len + c0) and the
+   * same slot count, stored slot by slot at bwd_tiles_offset with int32
+   * offsets [n_slots + 1] at bwd_slots_offset. Items with no queries or no
+   * keys have no backward tiles. */
+  int32_t block_n_bwd;
+  int32_t n_bwd_tiles;
+  uint64_t bwd_tiles_offset;
+  uint64_t bwd_slots_offset;
+  int64_t bwd_max_slot_cost;
 } zl_worklist_header; /* 128 bytes */
 
 int zl_abi_version(void);
@@ -171,6 +180,24 @@ int zl_merge_partials(int32_t n_parts, int64_t rows, int32_t num_heads, int32_t 
                       int32_t head_cnt, int32_t head_dim, const float* o_parts,
                       const float* lse_parts, int64_t part_row_stride, float* o_out,
                       float* lse_out, void* stream);
+
+/* Backward of the coalesced forward, recomputing the probabilities from the
+ * saved LSE (exact attention, pith.science review "Assumptions", Sec. II /
+ * FlashAttention [7]; the split of work over key/value blocks follows the
+ * theta k axis, "What carries the argument"). For every item and head, with
+ * P = exp(scale * q K^T - LSE):
+ *   D    = rowsum(dO * O)                 (written to d_ws, [q_rows, H] fp32)
+ *   dV  += P^T dO,   dS = P * (dO V^T - D)
+ *   dQ  += scale * dS K,   dK += scale * dS^T Q
+ * Gradients of items that share key/value rows add up. dq [q_rows, H, d],
+ * dk and dv [kv_rows, H, d] are fp32 and ACCUMULATED (the caller zeroes
+ * them); q, k, v, dout are bf16; o and lse are the forward's outputs. The
+ * sums use fp32 atomics, so the rounding order is not fixed between runs.
+ * Asynchronous on `stream`. Errors: ZL_ERR_NULL, ZL_ERR_WORKLIST,
+ * ZL_ERR_ALIGN, ZL_ERR_HIP. */
+int zl_coalesced_attn_bwd(const void* h_wl, const void* d_wl, const void* q, const void* k,
+                          const void* v, const float* o, const float* lse, const void* dout,
+                          float* dq, float* dk, float* dv, float* d_ws, void* stream);
 
 #ifdef __cplusplus
 }

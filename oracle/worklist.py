@@ -17,6 +17,11 @@ stable longest-processing-time-first (LPT) list schedule:
    least load so far (lowest slot index on ties). With n_slots == 0 the
    sorted order itself is the schedule (one workgroup per tile).
 
+The backward splits work the other way, along the key/value axis that a
+theta k split cuts (same section): a backward tile is ``block_n`` keys of
+one item on one head against all of the item's queries, cost = keys *
+q_len + c0, scheduled by the same rule.
+
 Python's ``sorted`` is stable and the slot search is a plain scan, so the
 result can be checked against the C++ builder bit for bit.
 """
@@ -49,11 +54,23 @@ def cut_tiles(items: Iterable, block_m: int, c0: int) -> List[Tile]:
     return tiles
 
 
-def lpt_schedule(items: Iterable, block_m: int, n_slots: int, c0: int
-                 ) -> Tuple[List[Tile], List[int], List[int]]:
-    """Returns (tiles in schedule order, slot_begin offsets [n_slots+1],
-    slot loads). For n_slots == 0: (tiles in LPT order, [], [])."""
-    tiles = cut_tiles(items, block_m, c0)
+def cut_bwd_tiles(items: Iterable, block_n: int, c0: int) -> List[Tile]:
+    tiles = []
+    for idx, it in enumerate(items):
+        q_off, q_len, kv_off, kv_len, h0, hc = (it.as_tuple() if hasattr(it, "as_tuple")
+                                                else tuple(int(x) for x in it))
+        if q_len == 0:
+            continue
+        for h in range(h0, h0 + hc):
+            for k0 in range(0, kv_len, block_n):
+                keys = min(block_n, kv_len - k0)
+                tiles.append(Tile(q_off, kv_off + k0, q_len, keys, h, idx, keys * q_len + c0))
+    return tiles
+
+
+def lpt(tiles: List[Tile], n_slots: int) -> Tuple[List[Tile], List[int], List[int]]:
+    """Stable LPT of already-cut tiles: (tiles in schedule order, slot_begin
+    offsets [n_slots+1], slot loads); for n_slots == 0 the LPT order."""
     order = sorted(tiles, key=lambda t: -t.cost)
     if n_slots == 0:
         return order, [], []
@@ -68,3 +85,16 @@ def lpt_schedule(items: Iterable, block_m: int, n_slots: int, c0: int
         flat += per_slot[s]
         begin.append(len(flat))
     return flat, begin, loads
+
+
+def lpt_schedule(items: Iterable, block_m: int, n_slots: int, c0: int
+                 ) -> Tuple[List[Tile], List[int], List[int]]:
+    """Forward schedule: (tiles in schedule order, slot_begin offsets
+    [n_slots+1], slot loads). For n_slots == 0: (tiles in LPT order, [], [])."""
+    return lpt(cut_tiles(items, block_m, c0), n_slots)
+
+
+def lpt_schedule_bwd(items: Iterable, block_n: int, n_slots: int, c0: int
+                     ) -> Tuple[List[Tile], List[int], List[int]]:
+    """Backward schedule over key blocks, same rule."""
+    return lpt(cut_bwd_tiles(items, block_n, c0), n_slots)

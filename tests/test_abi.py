@@ -11,7 +11,7 @@ import pytest
 
 from coalesced_attention_amd import workloads as W
 from coalesced_attention_amd import zl
-from oracle.worklist import lpt_schedule
+from oracle.worklist import lpt_schedule, lpt_schedule_bwd
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "zl.h")
@@ -57,6 +57,16 @@ def test_worklist_matches_reference_schedule(cfg, n_slots):
         assert list(built.slots()) == begin
         assert h.max_slot_cost == max(loads)
     assert h.total_cost == sum(t.cost for t in ref)
+    # backward: key blocks x heads x items, same LPT rule
+    c0_bwd = h.block_n_bwd * (h.cost_c0 // h.block_m)
+    bref, bbegin, bloads = lpt_schedule_bwd(wl.items, h.block_n_bwd, n_slots, c0_bwd)
+    bgot = built.bwd_tiles()
+    assert h.n_bwd_tiles == len(bref) == len(bgot)
+    bwant = np.array([(t.q_row0, t.kv_row0, t.q_rows, t.kv_len, t.head, t.item) for t in bref],
+                     dtype=zl.TILE_DTYPE)
+    assert np.array_equal(bgot, bwant)
+    if n_slots:
+        assert list(built.bwd_slots()) == bbegin and h.bwd_max_slot_cost == max(bloads)
 
 
 def test_worklist_is_deterministic():

@@ -1,0 +1,161 @@
+"""GPU parity of the recompute-from-LSE backward against the fp64 oracle,
+through the C ABI: dQ, dK, dV on the tiny workload (items sharing key/value
+rows), ragged shapes, and the training-step workload at full size."""
+
+import math
+
+import numpy as np
+import pytest
+
+from coalesced_attention_amd import workloads as W
+from oracle import attention as orc
+
+from gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+# Gradient gates: the forward's absolute bounds plus a per-tensor relative
+# L2 error (gradients of long items are small).
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+REL_L2 = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from coalesced_attention_amd import zl  # noqa: F401
+
+
+def _run(items, q, k, v, dout, H, d, n_slots=256):
+    from coalesced_attention_amd import zl
+    wl = zl.build_worklist(items, q.shape[0], k.shape[0], H, d, n_slots=n_slots, device=q.device)
+    o, lse = zl.coalesced_attn_fwd(wl, q, k, v)
+    dq, dk, dv = zl.coalesced_attn_bwd(wl, q, k, v, o, lse, dout)
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+
+
+class Gate:
+    def __init__(self, what):
+        self.what = what
+        self.stats = {}
+
+    def add(self, name, got, ref):
+        d = np.abs(got - ref)
+        s = self.stats.setdefault(name, [0.0, 0.0, 0, 0.0, 0.0])
+        s[0] = max(s[0], float(d.max(initial=0.0)))
+        s[1] += float(d.sum())
+        s[2] += d.size
+        s[3] += float((d ** 2).sum())
+        s[4] += float((ref ** 2).sum())
+
+    def check(self):
+        bad = []
+        for name, (mx, sm, n, num, den) in self.stats.items():
+            mean = sm / max(1, n)
+            rel = math.sqrt(num / den) if den > 0 else math.sqrt(num)
+            log(f"{self.what} {name}: max_abs={mx:.3e} mean_abs={mean:.3e} rel_l2={rel:.3e}")
+            if not (mx <= MAX_ABS and mean <= MEAN_ABS and rel <= REL_L2):
+                bad.append((name, mx, mean, rel))
+        assert not bad, (self.what, bad)
+
+
+def _oracle_all(items, Q, K, V, dO, scale):
+    return orc.coalesced_backward(Q, K, V, dO, items, scale)
+
+
+def test_backward_tiny_workload_shared_kv():
+    wl = W.config(0)
+    inp = W.make_inputs(wl)
+    q, k, v, g = (x.cuda() for x in (inp.q, inp.k, inp.v, inp.dout))
+    dq, dk, dv = _run(wl.items, q, k, v, g, wl.num_heads, wl.head_dim)
+    Qh, Kh, Vh, Gh = (x.double().numpy() for x in (inp.q, inp.k, inp.v, inp.dout))
+    rq, rk, rv = _oracle_all(wl.items, Qh, Kh, Vh, Gh, wl.softmax_scale)
+    gate = Gate("config 0 backward")
+    gate.add("dQ", dq, rq)
+    gate.add("dK", dk, rk)
+    gate.add("dV", dv, rv)
+    gate.check()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_ragged_and_head_splits(d):
+    H = 4
+    rng = np.random.default_rng(d + 1)
+    cases = [(1, 1), (63, 129), (64, 128), (65, 127), (200, 300), (130, 5), (7, 400)]
+    items, q_off, kv_off = [], 0, 0
+    for ql, kl in cases:
+        items.append(W.Item(q_off, ql, kv_off, kl, 0, H))
+        q_off += ql
+        kv_off += kl
+    items.append(W.Item(q_off, 90, 0, 300, 0, 2))      # shares keys with earlier items
+    items.append(W.Item(q_off, 90, 300, 150, 2, 2))    # head split of the same rows
+    q_off += 90
+    items.append(W.Item(q_off, 40, 0, 0, 0, H))        # no keys: O = 0, no gradient
+    items.append(W.Item(q_off + 40, 0, 0, 50, 0, H))   # no queries
+    q_off += 40
+    mk = lambda n: torch.from_numpy(rng.standard_normal((n, H, d)).astype(np.float32)).to(torch.bfloat16)
+    q, k, v, g = mk(q_off), mk(kv_off), mk(kv_off), mk(q_off)
+    dq, dk, dv = _run(items, q.cuda(), k.cuda(), v.cuda(), g.cuda(), H, d, n_slots=7)
+    rq, rk, rv = _oracle_all(items, q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                             g.double().numpy(), 1 / math.sqrt(d))
+    gate = Gate(f"ragged d={d} backward")
+    gate.add("dQ", dq, rq)
+    gate.add("dK", dk, rk)
+    gate.add("dV", dv, rv)
+    gate.check()
+
+
+@pytest.mark.timeout(900)
+def test_backward_training_step_full_size():
+    wl = W.config(4)
+    log("drawing inputs of config 4")
+    inp = W.make_inputs(wl)
+    q, k, v, g = (x.cuda() for x in (inp.q, inp.k, inp.v, inp.dout))
+    log("config 4: forward + backward on GPU")
+    dq, dk, dv = _run(wl.items, q, k, v, g, wl.num_heads, wl.head_dim)
+    assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
+    Qh, Kh, Vh, Gh = (x.float().numpy() for x in (inp.q, inp.k, inp.v, inp.dout))
+    s = wl.softmax_scale
+    gate = Gate("config 4 backward")
+    # every image item in full, every head
+    for it in wl.items[1:]:
+        for h in range(it.head_begin, it.head_begin + it.head_cnt):
+            qs, ks = slice(it.q_off, it.q_off + it.q_len), slice(it.kv_off, it.kv_off + it.kv_len)
+            rq, rk, rv, _, _ = orc.attention_backward_item(Qh[qs, h], Kh[ks, h], Vh[ks, h], Gh[qs, h], s)
+            gate.add("dQ", dq[qs, h], rq)
+            gate.add("dK", dk[ks, h], rk)
+            gate.add("dV", dv[ks, h], rv)
+    log("config 4: images checked; video shard heads 0 and 13")
+    it = wl.items[0]
+    for h in (0, 13):
+        qs, ks = slice(it.q_off, it.q_off + it.q_len), slice(it.kv_off, it.kv_off + it.kv_len)
+        rq, rk, rv, _, _ = orc.attention_backward_item(Qh[qs, h], Kh[ks, h], Vh[ks, h], Gh[qs, h], s)
+        gate.add("dQ", dq[qs, h], rq)
+        gate.add("dK", dk[ks, h], rk)
+        gate.add("dV", dv[ks, h], rv)
+        # the identities the oracle is pinned by hold on the GPU result too
+        assert np.abs(dk[ks, h].sum(0)).max() < 1e-2
+        np.testing.assert_allclose(dv[ks, h].sum(0), Gh[qs, h].sum(0), atol=2e-2, rtol=1e-3)
+    gate.check()
+
+
+def test_backward_accumulates_into_caller_buffers():
+    """dQ, dK, dV are sums into the caller's buffers: a second call adds the
+    same gradient again."""
+    from coalesced_attention_amd import zl
+    wl = W.config(0)
+    inp = W.make_inputs(wl)
+    q, k, v, g = (x.cuda() for x in (inp.q, inp.k, inp.v, inp.dout))
+    built = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim, device=q.device)
+    o, lse = zl.coalesced_attn_fwd(built, q, k, v)
+    once = [t.clone() for t in zl.coalesced_attn_bwd(built, q, k, v, o, lse, g)]
+    bufs = zl.coalesced_attn_bwd(built, q, k, v, o, lse, g)
+    twice = zl.coalesced_attn_bwd(built, q, k, v, o, lse, g, *bufs)
+    torch.cuda.synchronize()
+    for a, b in zip(once, twice):
+        torch.testing.assert_close(b, 2 * a, rtol=1e-5, atol=1e-6)

@@ -6,7 +6,7 @@ import itertools
 import numpy as np
 import pytest
 
-from oracle.worklist import cut_tiles, lpt_schedule
+from oracle.worklist import cut_bwd_tiles, cut_tiles, lpt_schedule, lpt_schedule_bwd
 
 
 def _items(rng, n):
@@ -79,3 +79,18 @@ def test_empty_and_zero_kv_items():
     tiles, begin, loads = lpt_schedule([(0, 0, 0, 5, 0, 1), (0, 10, 0, 0, 0, 1)], 128, 2, 7)
     assert len(tiles) == 1 and tiles[0].cost == 7 and tiles[0].kv_len == 0
     assert loads == [7, 0]
+
+
+def test_backward_tiles_cover_every_key_head_pair_once():
+    rng = np.random.default_rng(5)
+    items = _items(rng, 10)
+    tiles, begin, loads = lpt_schedule_bwd(items, 128, 5, 64)
+    cov = {}
+    for t in tiles:
+        assert t.kv_len <= 128 and t.cost == t.kv_len * t.q_rows + 64
+        for r in range(t.kv_row0, t.kv_row0 + t.kv_len):
+            cov[(t.item, r, t.head)] = cov.get((t.item, r, t.head), 0) + 1
+    want = {(i, it[2] + r, h) for i, it in enumerate(items) if it[1] > 0
+            for r in range(it[3]) for h in range(it[4], it[4] + it[5])}
+    assert set(cov) == want and set(cov.values()) == {1}
+    assert loads == [sum(t.cost for t in tiles[begin[s]:begin[s + 1]]) for s in range(5)]
