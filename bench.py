@@ -10,9 +10,12 @@ theta = (4, 1, 1) shard of a 32760-token video (8190 queries against all
 built once per batch on the host (timed separately) and reused, as every
 layer of a training step reuses it. Prints one JSON line.
 
-The KV-split merge (two 27450-row partials on 12 heads) is timed beside it
-and reported in GB/s. The cpu_baseline leg times the fp64 oracle on a
-bounded sample of the same workload on the host cores.
+The other steps of the path are timed beside it in the same run: the
+KV-split merge (two 27450-row partials on 12 heads, reported in GB/s) and
+the recompute-from-LSE backward of the same mix with an upstream gradient
+(reported in TFLOP/s under both flop conventions: 5 GEMMs = 2.5x the
+forward's flops, and 4 GEMMs = 2x). The cpu_baseline leg times the fp64
+oracle on a bounded sample of the same workload on the host cores.
 """
 
 from __future__ import annotations
@@ -39,6 +42,7 @@ def _args():
     ap.add_argument("--n-slots", type=int, default=-1, help="static slots (-1: one per CU, 0: one WG per tile)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (scale reference for FETCH/WRITE_SIZE)")
@@ -124,6 +128,45 @@ def _cpu_baseline(wl, inp, target_s):
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows_done} of {total_rows} (query row, head) pairs of the same workload "
                       f"({flops / 1e9:.1f} GFLOP in {el:.1f} s, fp64 numpy)"}
+
+
+def _bench_backward(zl, W, dev, stream, n_slots):
+    """Backward of the training-step mix (the mixed rank share plus dO):
+    forward once for O and LSE, then timed backward launches (D preprocess
+    and the key-block kernel) accumulating into zeroed fp32 gradients."""
+    import torch
+    wl = W.config(4)
+    inp = W.make_inputs(wl)
+    q, k, v, g = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.dout))
+    del inp
+    built = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim,
+                              n_slots=n_slots)
+    built.to(dev)
+    o, lse = zl.coalesced_attn_fwd(built, q, k, v, stream=stream)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.zeros(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.zeros(v.shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(lse.shape, dtype=torch.float32, device=dev)
+
+    def bwd():
+        zl.coalesced_attn_bwd(built, q, k, v, o, lse, g, dq, dk, dv, ws, stream=stream)
+
+    def zero():
+        dq.zero_()
+        dk.zero_()
+        dv.zero_()
+
+    for _ in range(2):
+        bwd()
+    torch.cuda.synchronize()
+    ms = _events_ms(bwd, 10, stream)
+    zms = _events_ms(zero, 10, stream)
+    F = wl.flops_fwd()
+    return {"workload": wl.name, "ms": round(ms, 4), "zero_grads_ms": round(zms, 4),
+            "TFLOP/s": round(2.5 * F / (ms * 1e-3) / 1e12, 2),
+            "TFLOP/s_4gemm": round(2.0 * F / (ms * 1e-3) / 1e12, 2),
+            "pct_of_peak": round(100 * 2.5 * F / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "flops_5gemm": 2.5 * F, "bwd_tiles": built.header.n_bwd_tiles}
 
 
 def main():
@@ -214,6 +257,9 @@ def main():
                         "GB/s": round(mbytes / (mms * 1e-3) / 1e9, 1),
                         "frac_of_hbm_peak": round(mbytes / (mms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                         "bytes": mbytes, "traffic": measured_traffic("merge_kernel<128>")}
+
+    if not a.no_bwd:
+        out["backward"] = _bench_backward(zl, W, dev, stream, n_slots)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(wl, inp, a.cpu_seconds)

@@ -2,15 +2,27 @@
 // probabilities from the forward's log-sum-exp.
 //
 // For every item and head, with s the softmax scale, P = exp(s q K^T - LSE):
-//   D  = rowsum(dO * O)                              (bwd_preprocess)
-//   dV += P^T dO,  dS = P * (dO V^T - D)
-//   dK += s dS^T Q,  dQ += s dS K                     (bwd_kernel)
+//   D  = rowsum(dO * O),  dS = s P (dO V^T - D)
+//   dQ += dS K                       (dq_kernel, one owner per query row)
+//   dV += P^T dO,  dK += dS^T Q      (dkdv_kernel, one owner per key block)
 // The attention is the dense exact attention of the pith.science review of
 // arXiv 2608.01150 ("Assumptions", Sec. II, after FlashAttention [7]); the
-// work is split over key/value blocks, the axis a theta k split cuts ("What
-// carries the argument").
+// dK/dV work is split over key/value blocks, the axis a theta k split cuts
+// ("What carries the argument").
 //
-// bwd_kernel: one tile = 128 keys of one item on one head, against all of the
+// Two kernels, no atomics on dQ: S and dP are recomputed by both (7 GEMMs in
+// all instead of 5), which costs less than summing a partial dQ from every
+// key block through device-scope fp32 atomics, and makes dQ deterministic.
+//
+// dq_kernel runs the forward's tiles (up to 256 query rows of one item on one
+// head, 8 waves x 32 rows) with the forward's layout: per 64-key block,
+//   S^T = K Q^T, dP^T = V dO^T       (A = K / V rows from LDS, B = Q^T / dO^T
+//                                     held in registers; lane = query)
+//   dS^T = s P^T (dP^T - D)          (in the accumulator registers)
+//   dQ^T += K^T dS^T                 (A = K^T transpose reads, B = dS^T)
+// It also computes D for its rows and stores it for dkdv_kernel.
+//
+// dkdv_kernel: one tile = 128 keys of one item on one head, against all of the
 // item's queries, 4 waves (one per SIMD) x 32 keys. A wave keeps its keys' K
 // and V rows in registers (as the B operands of S = Q K^T and dP = dO V^T) and
 // its dK^T and dV^T accumulators; the item's queries stream through LDS in
@@ -19,8 +31,6 @@
 //   S  = Q K^T, dP = dO V^T                    (A = Q / dO rows from LDS)
 //   P  = exp2(S c - LSE2), dS = s P (dP - D)   (lane = key, registers = queries)
 //   dV^T += dO^T P, dK^T += Q^T dS             (A = dO^T / Q^T transpose reads)
-//   dS^T -> LDS, barrier
-//   dQ[64 x 32-wide d slice] = dS K over all 128 keys -> fp32 atomics
 // At the end dK^T / dV^T go through LDS to coalesced fp32 atomics (items may
 // share key/value rows, whose gradients add up).
 
@@ -50,23 +60,33 @@ struct Bwd {
   static constexpr int kG = 512 / D;
   static constexpr int kGB = 1024 + 16 * kG;
   static constexpr int kQTile = (kBM / kG) * kGB;  // Q or dO rows of one step
-  static constexpr int kKTile = (kBN / kG) * kGB;  // K rows of the tile
-  // dS^T tile: kBN keys (rows) x kBM queries (columns), same scheme.
-  static constexpr int kG2 = 512 / kBM;
-  static constexpr int kGB2 = 1024 + 16 * kG2;
-  static constexpr int kSTile = (kBN / kG2) * kGB2;
   static constexpr int kOffQ = 0;                   // 2 stages
   static constexpr int kOffDO = 2 * kQTile;         // 2 stages
-  static constexpr int kOffK = 4 * kQTile;
-  static constexpr int kOffS = kOffK + kKTile;
-  static constexpr int kOffL = kOffS + kSTile;      // 2 stages x (LSE2[kBM], D[kBM]) fp32
+  static constexpr int kOffL = 4 * kQTile;          // 2 stages x (LSE2[kBM], D[kBM]) fp32
   static constexpr int kLdsBytes = kOffL + 2 * 2 * kBM * 4;
   // dK^T / dV^T flush: [kBN][D] fp32 with a 16-byte row pad, over the Q/dO area
   static constexpr int kFlushPitch = D * 4 + 16;
-  static constexpr int kUnits = kDB * kQB;           // dQ (d slice, query block) units
   static_assert(kBN == kWaves * 32 && kBM % 32 == 0, "shapes");
-  static_assert(kBN * kFlushPitch <= 4 * kQTile, "flush buffer fits the Q/dO stages");
-  static_assert(kUnits % kWaves == 0 || kWaves % kUnits == 0, "dQ units spread evenly");
+  static_assert(kBN * kFlushPitch <= kOffL, "flush buffer fits the Q/dO stages");
+};
+
+// dq_kernel: the forward's tile shape and LDS layout, 64-key blocks.
+template <int D>
+struct BwdQ {
+  static constexpr int kWaves = zl::kFwdWaves;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kBN = 64;
+  static constexpr int kKB = kBN / 32;
+  static constexpr int kDS = D / 16;
+  static constexpr int kDB = D / 32;
+  static constexpr int kG = 512 / D;
+  static constexpr int kGB = 1024 + 16 * kG;
+  static constexpr int kGroups = kBN / kG;
+  static constexpr int kTileBytes = kGroups * kGB;
+  static constexpr int kStages = 3;
+  static constexpr int kLdsBytes = 2 * kStages * kTileBytes;
+  static constexpr int kGroupsPerWave = (kGroups + kWaves - 1) / kWaves;
+  static_assert(zl::kFwdBlockM == kWaves * 32, "forward tiles hold 32 rows per wave");
 };
 
 // Byte offset of the 16-byte chunk holding (row, col) in a group-layout tile
@@ -75,47 +95,215 @@ __device__ __forceinline__ int grp_off(int row, int col, int G, int GB) {
   return (row / G) * GB + ((col / 8) * G + row % G) * 16;
 }
 
-// ---------------------------------------------------------------- preprocess
-// D[row, head] = sum_c dO[row, head, c] * O[row, head, c] over the forward
-// tiles (256 rows x 1 head each): one thread per row.
+// ---------------------------------------------------------------- dQ
 template <int D>
-__global__ __launch_bounds__(256) void bwd_preprocess(const zl_tile* __restrict__ tiles,
-                                                      const __bf16* __restrict__ dO,
-                                                      const float* __restrict__ O,
-                                                      float* __restrict__ Dws, int H) {
-  const zl_tile t = uniform_tile(tiles[blockIdx.x]);
-  const int r = threadIdx.x;
-  if (r >= t.q_rows) return;
-  const int64_t row = t.q_row0 + r;
-  const __bf16* g = dO + (row * H + t.head) * D;
-  const float* o = O + (row * H + t.head) * D;
-  float acc = 0.f;
+__device__ __forceinline__ void dq_tile(const zl_tile& tile, const __bf16* __restrict__ Q,
+                                        const __bf16* __restrict__ K,
+                                        const __bf16* __restrict__ V,
+                                        const __bf16* __restrict__ dO,
+                                        const float* __restrict__ O,
+                                        const float* __restrict__ LSE, float* __restrict__ Dws,
+                                        float* __restrict__ dQ, int H, float scale,
+                                        char ZL_LDS* smem) {
+  using C = BwdQ<D>;
+  constexpr int KB = C::kKB, DS = C::kDS, DB = C::kDB, G = C::kG, GB = C::kGB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+  const int64_t rs = int64_t(H) * D;
+  const float c = scale * kLog2e;
+
+  // ---- this lane's query row: Q^T and dO^T fragments (head_dim
+  // [ds*16 + 8*half, +8)), D = rowsum(dO * O) and LSE in exp2 units
+  const int qr = wave * 32 + l32;
+  const bool qvalid = qr < tile.q_rows;
+  const int64_t row = tile.q_row0 + (qvalid ? qr : 0);
+  bf16x8 qf[DS], gf[DS];
+  float dpart = 0.f;
+  {
+    const int64_t off = row * rs + int64_t(tile.head) * D + 8 * half;
 #pragma unroll
-  for (int c = 0; c < D; c += 8) {
-    const bf16x8 gv = *reinterpret_cast<const bf16x8*>(g + c);
-    const f32x4 o0 = *reinterpret_cast<const f32x4*>(o + c);
-    const f32x4 o1 = *reinterpret_cast<const f32x4*>(o + c + 4);
+    for (int ds = 0; ds < DS; ++ds) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(Q + off + ds * 16);
+      const bf16x8 g = *reinterpret_cast<const bf16x8*>(dO + off + ds * 16);
+      const f32x4 o0 = *reinterpret_cast<const f32x4*>(O + off + ds * 16);
+      const f32x4 o1 = *reinterpret_cast<const f32x4*>(O + off + ds * 16 + 4);
+      qf[ds] = qvalid ? x : bf16x8{};
+      gf[ds] = qvalid ? g : bf16x8{};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc = fmaf(float(gv[e]), o0[e], acc);
+      for (int e = 0; e < 4; ++e) dpart = fmaf(float(g[e]), o0[e], dpart);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc = fmaf(float(gv[4 + e]), o1[e], acc);
+      for (int e = 0; e < 4; ++e) dpart = fmaf(float(g[4 + e]), o1[e], dpart);
+    }
   }
-  Dws[row * H + t.head] = acc;
+  const float drow = qvalid ? swap_halves_sum(dpart) : 0.f;
+  const float l2 = qvalid ? LSE[row * H + tile.head] * kLog2e : INFINITY;
+  if (qvalid && half == 0) Dws[row * H + tile.head] = drow;
+
+  const int kv_len = tile.kv_len;
+  const int nblk = (kv_len + C::kBN - 1) / C::kBN;
+  const __bf16* kbase = K + tile.kv_row0 * rs + int64_t(tile.head) * D;
+  const __bf16* vbase = V + tile.kv_row0 * rs + int64_t(tile.head) * D;
+
+  // ---- direct-to-LDS loads of key block `blk` (rows past kv_len read as 0)
+  const int ld_lane = (lane % G) * int(rs) * 2 + (lane / G) * 16;
+  auto issue_tile = [&](const __bf16* base, int stage_off, int blk) __attribute__((always_inline)) {
+    const int rows = min(C::kBN, max(0, kv_len - blk * C::kBN));
+    const int64_t addr = uniform_i64(reinterpret_cast<int64_t>(base + int64_t(blk) * C::kBN * rs));
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<__bf16*>(addr), 0,
+                                                        __builtin_amdgcn_readfirstlane(rows * int(rs) * 2),
+                                                        kBufferFlags);
+#pragma unroll
+    for (int i = 0; i < C::kGroupsPerWave; ++i) {
+      const int gi = wave * C::kGroupsPerWave + i;
+      if (C::kGroups % (C::kWaves * C::kGroupsPerWave) != 0 && gi >= C::kGroups) break;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (void ZL_LDS*)(smem + stage_off + gi * GB), 16, ld_lane,
+          __builtin_amdgcn_readfirstlane(gi * G * int(rs) * 2), 0, 0);
+    }
+  };
+  constexpr int kLoadsPerTile = C::kGroupsPerWave;
+  auto kstage = [&](int blk) { return (blk % C::kStages) * C::kTileBytes; };
+  auto vstage = [&](int blk) { return (C::kStages + blk % C::kStages) * C::kTileBytes; };
+
+  // row fragment (A of S^T and dP^T): row b*32 + l32, chunk 2*ds + half
+  const int r_lane = (l32 / G) * GB + (half * G + l32 % G) * 16;
+  // K^T fragment by transpose reads (A of dQ^T), as the forward's V^T
+  const int rr = 4 * half + ((lane & 15) >> 2);
+  const int c_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int t_lane = (rr / G) * GB + (c_l * G + rr % G) * 16 + (lane & 1) * 8;
+  auto opaque = [&](int a) __attribute__((always_inline)) {
+    asm volatile("" : "+v"(a));
+    return (const char ZL_LDS*)(smem + a);
+  };
+  auto read_row = [&](const char ZL_LDS* base, int b, int ds) __attribute__((always_inline)) {
+    return lds_read_b128(base + (b * 32 / G) * GB + ds * 2 * G * 16);
+  };
+  auto read_tr = [&](const char ZL_LDS* base, int b, int u, int db) __attribute__((always_inline)) {
+    const char ZL_LDS* p = base + ((b * 32 + 16 * u) / G) * GB + db * 4 * G * 16;
+    const i16x4 lo = lds_read_tr16(p);
+    const i16x4 hi = lds_read_tr16(p + (8 / G) * GB + (8 % G) * 16);  // 8 rows further
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
+
+  if (nblk > 0) {
+    issue_tile(kbase, kstage(0), 0);
+    issue_tile(vbase, vstage(0), 0);
+    issue_tile(kbase, kstage(1), 1);
+    issue_tile(vbase, vstage(1), 1);
+  }
+  for (int j = 0; j < nblk; ++j) {
+    // K(j), V(j) are older than the two loads of block j + 1
+    __builtin_amdgcn_s_waitcnt(kWaitLoads + 2 * kLoadsPerTile);
+    __syncthreads();  // every wave's part of block j has landed; block j - 1 is no longer read
+    issue_tile(kbase, kstage(j + 2), j + 2);
+    issue_tile(vbase, vstage(j + 2), j + 2);
+    const char ZL_LDS* kr = opaque(kstage(j) + r_lane);
+    const char ZL_LDS* vr = opaque(vstage(j) + r_lane);
+    const char ZL_LDS* kt = opaque(kstage(j) + t_lane);
+
+    // S^T and dP^T: lane = query, register r = key b*32 + 8(r/4) + 4*half + r%4
+    f32x16 s[KB], dp[KB];
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+      s[b] = f32x16{};
+      dp[b] = f32x16{};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row(kr, b, ds), qf[ds], s[b], 0, 0, 0);
+        dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row(vr, b, ds), gf[ds], dp[b], 0, 0, 0);
+      }
+    }
+    const bool last_ragged = j + 1 == nblk && (kv_len % C::kBN) != 0;
+    // dS^T in bf16; k-slot e of operand (b, u) is key b*32 + 16u + 8(e/4) + 4*half + e%4
+    bf16x8 dsb[KB][2];
+#pragma unroll
+    for (int b = 0; b < KB; ++b)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * u + e;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -l2));
+          if (last_ragged) {
+            const int key = j * C::kBN + b * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (key >= kv_len) p = 0.f;
+          }
+          dsb[b][u][e] = (__bf16)((dp[b][r] - drow) * (p * scale));
+        }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int b = 0; b < KB; ++b)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(kt, b, u, db), dsb[b][u], dq[db], 0, 0, 0);
+  }
+
+  // ---- dQ += dQ^T (lane = query, register r = d db*32 + 8(r/4) + 4*half + r%4);
+  // the tile is the only writer of these (row, head) pairs
+  if (qvalid) {
+    float* qp = dQ + row * rs + int64_t(tile.head) * D + 4 * half;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4* p = reinterpret_cast<f32x4*>(qp + db * 32 + 8 * g);
+        const f32x4 a = {dq[db][4 * g], dq[db][4 * g + 1], dq[db][4 * g + 2], dq[db][4 * g + 3]};
+        *p = *p + a;
+      }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(BwdQ<D>::kThreads, 1) void dq_kernel(
+    const zl_tile* __restrict__ tiles, const int32_t* __restrict__ slots, int n_slots,
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const float* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ Dws, float* __restrict__ dQ, int H, float scale) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[BwdQ<D>::kLdsBytes];
+  char ZL_LDS* smem = (char ZL_LDS*)(smem_raw);
+  int t0, t1;
+  if (n_slots > 0) {
+    // the forward's XCD-aware slot mapping: the query blocks of one (item,
+    // head), which read the same K/V, share an L2
+    const int w = blockIdx.x;
+    const int s = n_slots % kXcds == 0 ? (w % kXcds) * (n_slots / kXcds) + w / kXcds : w;
+    t0 = slots[s];
+    t1 = slots[s + 1];
+  } else {
+    t0 = blockIdx.x;
+    t1 = t0 + 1;
+  }
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  t1 = __builtin_amdgcn_readfirstlane(t1);
+  for (int t = t0; t < t1; ++t) {
+    const zl_tile tile = uniform_tile(tiles[t]);
+    dq_tile<D>(tile, Q, K, V, dO, O, LSE, Dws, dQ, H, scale, smem);
+    __builtin_amdgcn_s_waitcnt(0);  // the zero-filled prefetches of blocks past the end
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------- main
 template <int D>
-__device__ __forceinline__ void bwd_tile(const zl_tile& tile, const __bf16* __restrict__ Q,
-                                         const __bf16* __restrict__ K,
-                                         const __bf16* __restrict__ V,
-                                         const __bf16* __restrict__ dO,
-                                         const float* __restrict__ LSE,
-                                         const float* __restrict__ Dws, float* __restrict__ dQ,
-                                         float* __restrict__ dK, float* __restrict__ dV, int H,
-                                         float scale, char ZL_LDS* smem) {
+__device__ __forceinline__ void dkdv_tile(const zl_tile& tile, const __bf16* __restrict__ Q,
+                                          const __bf16* __restrict__ K,
+                                          const __bf16* __restrict__ V,
+                                          const __bf16* __restrict__ dO,
+                                          const float* __restrict__ LSE,
+                                          const float* __restrict__ Dws, float* __restrict__ dK,
+                                          float* __restrict__ dV, int H, float scale,
+                                          char ZL_LDS* smem) {
   using C = Bwd<D>;
   constexpr int DS = C::kDS, DB = C::kDB, QB = C::kQB, G = C::kG, GB = C::kGB;
-  constexpr int G2 = C::kG2, GB2 = C::kGB2;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -184,9 +372,6 @@ __device__ __forceinline__ void bwd_tile(const zl_tile& tile, const __bf16* __re
   const int e_l = (lane & 15) >> 2;
   const int c_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int tq_lane = ((4 * half + e_l) / G) * GB + (c_l * G + (4 * half + e_l) % G) * 16 + (lane & 1) * 8;
-  // transpose reads in natural order (dQ GEMM): rows 8*half + e (+4)
-  const int tk_lane = ((8 * half + e_l) / G) * GB + (c_l * G + (8 * half + e_l) % G) * 16 + (lane & 1) * 8;
-  const int ts_lane = ((8 * half + e_l) / G2) * GB2 + (c_l * G2 + (8 * half + e_l) % G2) * 16 + (lane & 1) * 8;
 
   auto tr8 = [&](const char ZL_LDS* p0, const char ZL_LDS* p1) __attribute__((always_inline)) {
     const i16x4 lo = lds_read_tr16(p0);
@@ -195,8 +380,6 @@ __device__ __forceinline__ void bwd_tile(const zl_tile& tile, const __bf16* __re
   };
   // Row r0 + 8 in a group layout is (8 / G) groups and (8 % G) rows further.
   constexpr int kPlus8 = (8 / G) * GB + (8 % G) * 16;
-  constexpr int kPlus4 = (4 / G) * GB + (4 % G) * 16;
-  constexpr int kPlus4S = (4 / G2) * GB2 + (4 % G2) * 16;
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -206,8 +389,7 @@ __device__ __forceinline__ void bwd_tile(const zl_tile& tile, const __bf16* __re
   }
 
   const int nsteps = (tile.q_rows + C::kBM - 1) / C::kBM;
-  // ---- prologue: K tile, step 0 of Q / dO / LSE / D
-  issue_rows(K, tile.kv_row0, tile.kv_len, C::kBN, C::kOffK);
+  // ---- prologue: step 0 of Q / dO / LSE / D
   issue_rows(Q, tile.q_row0, tile.q_rows, C::kBM, C::kOffQ);
   issue_rows(dO, tile.q_row0, tile.q_rows, C::kBM, C::kOffDO);
   store_ld(0, load_ld(0));
@@ -281,52 +463,8 @@ __device__ __forceinline__ void bwd_tile(const zl_tile& tile, const __bf16* __re
                                                            dk[db], 0, 0, 0);
         }
 
-    // ---- dS^T -> LDS: row = key; elements 0-3 / 4-7 of sf[qb][u] are the
-    // queries qb*32 + 16u + 4h .. +3 / qb*32 + 16u + 8 + 4h .. +3. The halves
-    // are split with whole-vector shuffles: building the stored vector from
-    // single bf16 elements is lowered to a lossy byte permute.
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const i16x8 all = __builtin_bit_cast(i16x8, sf[qb][u]);
-        const i16x4 lo = __builtin_shufflevector(all, all, 0, 1, 2, 3);
-        const i16x4 hi = __builtin_shufflevector(all, all, 4, 5, 6, 7);
-        const int off = grp_off(key, qb * 32 + 16 * u, G2, GB2) + half * 8;
-        *reinterpret_cast<i16x4 ZL_LDS*>(smem + C::kOffS + off) = lo;
-        *reinterpret_cast<i16x4 ZL_LDS*>(smem + C::kOffS + off + G2 * 16) = hi;  // next chunk
-      }
-    // The next step's direct loads were issued before this step's MFMAs; every
-    // wave waits for its own before the barrier, so after it they are all in LDS.
+    // the next step's direct loads were issued at the top of this step
     __builtin_amdgcn_s_waitcnt(kWaitLoads);
-    __syncthreads();
-
-    // ---- dQ = dS K for (d slice, query block) units, over all 128 keys
-    const char ZL_LDS* ks = smem + C::kOffK;
-    const char ZL_LDS* ss = smem + C::kOffS;
-#pragma unroll
-    for (int n = 0; n < (C::kUnits + C::kWaves - 1) / C::kWaves; ++n) {
-      const int unit = wave + n * C::kWaves;
-      if (C::kUnits % C::kWaves != 0 && unit >= C::kUnits) break;
-      const int db = unit % DB, qb = unit / DB;
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < C::kBN / 16; ++kk) {
-        const int koff = ((kk * 16) / G) * GB + tk_lane + db * 4 * G * 16;
-        const int soff = ((kk * 16) / G2) * GB2 + ts_lane + qb * 4 * G2 * 16;
-        const bf16x8 a = tr8(ss + soff, ss + soff + kPlus4S);
-        const bf16x8 b = tr8(ks + koff, ks + koff + kPlus4);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-      }
-      // lane = d column db*32 + l32, register r = query qb*32 + 8(r/4) + 4h + r%4
-      const int d = db * 32 + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = step * C::kBM + qb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (qr < tile.q_rows)
-          atomicAdd(dQ + ((tile.q_row0 + qr) * H + tile.head) * D + d, acc[r]);
-      }
-    }
     if (more) store_ld(st ^ 1, ld_next);
     __syncthreads();
   }
@@ -355,18 +493,21 @@ __device__ __forceinline__ void bwd_tile(const zl_tile& tile, const __bf16* __re
 }
 
 template <int D>
-__global__ __launch_bounds__(Bwd<D>::kThreads, 1) void bwd_kernel(
+__global__ __launch_bounds__(Bwd<D>::kThreads, 1) void dkdv_kernel(
     const zl_tile* __restrict__ tiles, const int32_t* __restrict__ slots, int n_slots,
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dws,
-    float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int H, float scale) {
+    float* __restrict__ dK, float* __restrict__ dV, int H, float scale) {
   __shared__ __attribute__((aligned(16))) char smem_raw[Bwd<D>::kLdsBytes];
   char ZL_LDS* smem = (char ZL_LDS*)(smem_raw);  // generic -> LDS address space
   int t0, t1;
   if (n_slots > 0) {
-    // same XCD-aware slot mapping as the forward
-    const int w = blockIdx.x;
-    const int s = n_slots % kXcds == 0 ? (w % kXcds) * (n_slots / kXcds) + w / kXcds : w;
+    // Slot = workgroup. Workgroups go round-robin to the 8 XCDs, and equal-cost
+    // backward tiles are cut key block by key block with the heads innermost,
+    // so when the head count and the slot count are multiples of 8, XCD x runs
+    // every key block of heads x, x + 8, ...: the Q / dO rows those tiles
+    // stream stay in one L2.
+    const int s = blockIdx.x;
     t0 = slots[s];
     t1 = slots[s + 1];
   } else {
@@ -377,7 +518,7 @@ __global__ __launch_bounds__(Bwd<D>::kThreads, 1) void bwd_kernel(
   t1 = __builtin_amdgcn_readfirstlane(t1);
   for (int t = t0; t < t1; ++t) {
     const zl_tile tile = uniform_tile(tiles[t]);
-    bwd_tile<D>(tile, Q, K, V, dO, LSE, Dws, dQ, dK, dV, H, scale, smem);
+    dkdv_tile<D>(tile, Q, K, V, dO, LSE, Dws, dK, dV, H, scale, smem);
     __syncthreads();
   }
 }
@@ -386,23 +527,28 @@ template <int D>
 int launch_bwd(const zl_worklist_header* h, const char* d_wl, const void* q, const void* k,
                const void* v, const float* o, const float* lse, const void* dout, float* dq,
                float* dk, float* dv, float* d_ws, hipStream_t stream) {
-  if (h->n_tiles > 0) {
-    hipLaunchKernelGGL(bwd_preprocess<D>, dim3(h->n_tiles), dim3(256), 0, stream,
+  const __bf16* Q = static_cast<const __bf16*>(q);
+  const __bf16* K = static_cast<const __bf16*>(k);
+  const __bf16* V = static_cast<const __bf16*>(v);
+  const __bf16* G = static_cast<const __bf16*>(dout);
+  // dQ and D over the forward's tiles and slots, then dK / dV (which read D)
+  const int qgrid = h->n_slots > 0 ? h->n_slots : h->n_tiles;
+  if (qgrid > 0 && h->n_tiles > 0) {
+    hipLaunchKernelGGL(dq_kernel<D>, dim3(qgrid), dim3(BwdQ<D>::kThreads), 0, stream,
                        reinterpret_cast<const zl_tile*>(d_wl + h->tiles_offset),
-                       static_cast<const __bf16*>(dout), o, d_ws, h->num_heads);
+                       reinterpret_cast<const int32_t*>(d_wl + h->slots_offset), h->n_slots, Q, K,
+                       V, G, o, lse, d_ws, dq, h->num_heads, h->softmax_scale);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return zl::fail(ZL_ERR_HIP, "backward preprocess launch: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return zl::fail(ZL_ERR_HIP, "backward dQ launch: %s", hipGetErrorString(e));
   }
   const int grid = h->n_slots > 0 ? h->n_slots : h->n_bwd_tiles;
   if (grid == 0 || h->n_bwd_tiles == 0) return ZL_OK;
-  hipLaunchKernelGGL(bwd_kernel<D>, dim3(grid), dim3(Bwd<D>::kThreads), 0, stream,
+  hipLaunchKernelGGL(dkdv_kernel<D>, dim3(grid), dim3(Bwd<D>::kThreads), 0, stream,
                      reinterpret_cast<const zl_tile*>(d_wl + h->bwd_tiles_offset),
-                     reinterpret_cast<const int32_t*>(d_wl + h->bwd_slots_offset), h->n_slots,
-                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), static_cast<const __bf16*>(dout), lse, d_ws,
-                     dq, dk, dv, h->num_heads, h->softmax_scale);
+                     reinterpret_cast<const int32_t*>(d_wl + h->bwd_slots_offset), h->n_slots, Q,
+                     K, V, G, lse, d_ws, dk, dv, h->num_heads, h->softmax_scale);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return zl::fail(ZL_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return zl::fail(ZL_ERR_HIP, "backward dK/dV launch: %s", hipGetErrorString(e));
   return ZL_OK;
 }
 

@@ -136,16 +136,19 @@ struct TileKey {
   int64_t cost;
 };
 
-// Stable LPT: order by cost, largest first, equal costs in cut order (item,
-// head, first row) -- a total order, so std::sort gives the stable result.
+// Stable LPT: order by cost, largest first, equal costs in cut order -- a
+// total order, so std::sort gives the stable result. Forward tiles are cut
+// in (item, head, first query row) order; backward tiles (kv_first) in
+// (item, first key row, head) order.
 // With n_slots == 0 the order itself is written; otherwise each tile goes to
 // the least-loaded slot (lowest index on ties) and the tiles are written slot
 // by slot with offsets [n_slots + 1].
 int schedule(std::vector<TileKey>& tiles, int32_t n_slots, zl_tile* out, int32_t* slots,
-             int64_t* total_cost, int64_t* makespan) {
-  std::sort(tiles.begin(), tiles.end(), [](const TileKey& a, const TileKey& b) {
+             int64_t* total_cost, int64_t* makespan, bool kv_first = false) {
+  std::sort(tiles.begin(), tiles.end(), [kv_first](const TileKey& a, const TileKey& b) {
     if (a.cost != b.cost) return a.cost > b.cost;
     if (a.t.item != b.t.item) return a.t.item < b.t.item;
+    if (kv_first && a.t.kv_row0 != b.t.kv_row0) return a.t.kv_row0 < b.t.kv_row0;
     if (a.t.head != b.t.head) return a.t.head < b.t.head;
     if (a.t.q_row0 != b.t.q_row0) return a.t.q_row0 < b.t.q_row0;
     return a.t.kv_row0 < b.t.kv_row0;
@@ -271,19 +274,19 @@ extern "C" int zl_build_worklist(const zl_problem* problem, const zl_item* items
     for (int32_t i = 0; i < n_items; ++i) {
       const zl_item& it = items[i];
       if (it.q_len == 0) continue;
-      for (int32_t h = it.head_begin; h < it.head_begin + it.head_cnt; ++h)
-        for (int32_t k0 = 0; k0 < it.kv_len; k0 += kBwdBlockN) {
-          const int32_t keys = std::min(kBwdBlockN, it.kv_len - k0);
+      for (int32_t k0 = 0; k0 < it.kv_len; k0 += kBwdBlockN) {
+        const int32_t keys = std::min(kBwdBlockN, it.kv_len - k0);
+        for (int32_t h = it.head_begin; h < it.head_begin + it.head_cnt; ++h)
           btiles.push_back(TileKey{zl_tile{it.q_off, it.kv_off + k0, it.q_len, keys, h, i},
                                    int64_t(keys) * it.q_len + c0_bwd});
-        }
+      }
     }
   } catch (const std::bad_alloc&) {
     return fail(ZL_ERR_ARG, "out of host memory for %d backward tiles", n_bwd_tiles);
   }
   int64_t bwd_total = 0, bwd_makespan = 0;
   rc = schedule(btiles, n_slots, reinterpret_cast<zl_tile*>(base + bwd_tiles_off),
-                reinterpret_cast<int32_t*>(base + bwd_slots_off), &bwd_total, &bwd_makespan);
+                reinterpret_cast<int32_t*>(base + bwd_slots_off), &bwd_total, &bwd_makespan, true);
   if (rc) return rc;
 
   hdr->magic = ZL_WORKLIST_MAGIC;

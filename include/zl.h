@@ -119,10 +119,11 @@ typedef struct zl_worklist_header {
   int64_t total_cost;
   int64_t max_slot_cost; /* makespan of the static schedule (0 if n_slots == 0) */
   /* Backward tiles: block_n_bwd keys of one item on one head, against all of
-   * the item's query rows; same LPT rule (cost = q_rows * kv_len + c0) and the
-   * same slot count, stored slot by slot at bwd_tiles_offset with int32
-   * offsets [n_slots + 1] at bwd_slots_offset. Items with no queries or no
-   * keys have no backward tiles. */
+   * the item's query rows; same LPT rule (cost = q_rows * kv_len + c0), with
+   * equal costs kept in (item, key block, head) order, and the same slot
+   * count, stored slot by slot at bwd_tiles_offset with int32 offsets
+   * [n_slots + 1] at bwd_slots_offset. Slot s runs on workgroup s. Items with
+   * no queries or no keys have no backward tiles. */
   int32_t block_n_bwd;
   int32_t n_bwd_tiles;
   uint64_t bwd_tiles_offset;
@@ -183,18 +184,19 @@ int zl_merge_partials(int32_t n_parts, int64_t rows, int32_t num_heads, int32_t 
 
 /* Backward of the coalesced forward, recomputing the probabilities from the
  * saved LSE (exact attention, pith.science review "Assumptions", Sec. II /
- * FlashAttention [7]; the split of work over key/value blocks follows the
- * theta k axis, "What carries the argument"). For every item and head, with
- * P = exp(scale * q K^T - LSE):
+ * FlashAttention [7]; the split of the dK / dV work over key/value blocks
+ * follows the theta k axis, "What carries the argument"). For every item and
+ * head, with P = exp(scale * q K^T - LSE):
  *   D    = rowsum(dO * O)                 (written to d_ws, [q_rows, H] fp32)
  *   dV  += P^T dO,   dS = P * (dO V^T - D)
  *   dQ  += scale * dS K,   dK += scale * dS^T Q
- * Gradients of items that share key/value rows add up. dq [q_rows, H, d],
- * dk and dv [kv_rows, H, d] are fp32 and ACCUMULATED (the caller zeroes
- * them); q, k, v, dout are bf16; o and lse are the forward's outputs. The
- * sums use fp32 atomics, so the rounding order is not fixed between runs.
- * Asynchronous on `stream`. Errors: ZL_ERR_NULL, ZL_ERR_WORKLIST,
- * ZL_ERR_ALIGN, ZL_ERR_HIP. */
+ * dq [q_rows, H, d], dk and dv [kv_rows, H, d] are fp32 and ACCUMULATED
+ * (the caller zeroes them); q, k, v, dout are bf16; o and lse are the
+ * forward's outputs. Two launches on `stream`: dQ and D over the forward
+ * tiles (each (row, head) has one writer: deterministic), then dK / dV over
+ * the backward tiles, added with fp32 atomics because items may share
+ * key/value rows (where they do, the order of those sums is not fixed).
+ * Errors: ZL_ERR_NULL, ZL_ERR_WORKLIST, ZL_ERR_ALIGN, ZL_ERR_HIP. */
 int zl_coalesced_attn_bwd(const void* h_wl, const void* d_wl, const void* q, const void* k,
                           const void* v, const float* o, const float* lse, const void* dout,
                           float* dq, float* dk, float* dv, float* d_ws, void* stream);

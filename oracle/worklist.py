@@ -20,7 +20,8 @@ stable longest-processing-time-first (LPT) list schedule:
 The backward splits work the other way, along the key/value axis that a
 theta k split cuts (same section): a backward tile is ``block_n`` keys of
 one item on one head against all of the item's queries, cost = keys *
-q_len + c0, scheduled by the same rule.
+q_len + c0, scheduled by the same rule. Its tiles are cut in the order
+(item, key block, head), so equal-cost ties run through the heads first.
 
 Python's ``sorted`` is stable and the slot search is a plain scan, so the
 result can be checked against the C++ builder bit for bit.
@@ -61,9 +62,9 @@ def cut_bwd_tiles(items: Iterable, block_n: int, c0: int) -> List[Tile]:
                                                 else tuple(int(x) for x in it))
         if q_len == 0:
             continue
-        for h in range(h0, h0 + hc):
-            for k0 in range(0, kv_len, block_n):
-                keys = min(block_n, kv_len - k0)
+        for k0 in range(0, kv_len, block_n):
+            keys = min(block_n, kv_len - k0)
+            for h in range(h0, h0 + hc):
                 tiles.append(Tile(q_off, kv_off + k0, q_len, keys, h, idx, keys * q_len + c0))
     return tiles
 
