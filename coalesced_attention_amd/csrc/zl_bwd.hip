@@ -22,17 +22,20 @@
 //   dQ^T += K^T dS^T                 (A = K^T transpose reads, B = dS^T)
 // It also computes D for its rows and stores it for dkdv_kernel.
 //
-// dkdv_kernel: one tile = 128 keys of one item on one head, against all of the
-// item's queries, 4 waves (one per SIMD) x 32 keys. A wave keeps its keys' K
-// and V rows in registers (as the B operands of S = Q K^T and dP = dO V^T) and
-// its dK^T and dV^T accumulators; the item's queries stream through LDS in
-// steps of 64 rows (Q, dO, and their LSE and D), double-buffered with
-// direct-to-LDS loads. Per step and wave:
-//   S  = Q K^T, dP = dO V^T                    (A = Q / dO rows from LDS)
-//   P  = exp2(S c - LSE2), dS = s P (dP - D)   (lane = key, registers = queries)
-//   dV^T += dO^T P, dK^T += Q^T dS             (A = dO^T / Q^T transpose reads)
-// At the end dK^T / dV^T go through LDS to coalesced fp32 atomics (items may
-// share key/value rows, whose gradients add up).
+// dkdv_kernel: one tile = 128 keys of one item on one head, against all of
+// the item's queries, streamed through LDS 32 rows at a time (Q, dO, LSE, D;
+// direct-to-LDS loads, a 4-step ring, two steps ahead). 8 waves in 4
+// producer / consumer pairs, one of each per SIMD, 32 keys per pair:
+//   producer: K, V rows of its keys in registers (B operands);
+//             S = Q K^T, dP = dO V^T (A = Q / dO rows; lane = key),
+//             P = exp2(S c - LSE2), dS = s P (dP - D), packed to bf16 and
+//             written to an LDS exchange buffer exactly as held in registers
+//   consumer: one step behind, dV^T += dO^T P, dK^T += Q^T dS (A = dO^T /
+//             Q^T transpose reads, B = the producer's registers from LDS);
+//             holds the dK^T / dV^T accumulators
+// so the exponentials of one wave run beside the MFMAs of the other. One
+// barrier per step. At the end dK^T / dV^T go through LDS to coalesced fp32
+// atomics (items may share key/value rows, whose gradients add up).
 
 #include <hip/hip_runtime.h>
 
@@ -48,26 +51,36 @@ using namespace zl::dev;
 
 template <int D>
 struct Bwd {
-  static constexpr int kWaves = zl::kBwdWaves;
+  static constexpr int kPairs = zl::kBwdPairs;
+  static constexpr int kWaves = 2 * kPairs;
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kBN = zl::kBwdBlockN;  // keys per tile, 32 per wave
+  static constexpr int kBN = zl::kBwdBlockN;  // keys per tile, 32 per pair
   static constexpr int kBM = zl::kBwdBlockM;  // query rows per step
-  static constexpr int kQB = kBM / 32;
   static constexpr int kDS = D / 16;
   static constexpr int kDB = D / 32;
   // bf16 tiles with D columns use the forward's group layout: kG rows of
   // 1 KB stored chunk-column-major, each group padded by 16*kG bytes.
   static constexpr int kG = 512 / D;
   static constexpr int kGB = 1024 + 16 * kG;
-  static constexpr int kQTile = (kBM / kG) * kGB;  // Q or dO rows of one step
-  static constexpr int kOffQ = 0;                   // 2 stages
-  static constexpr int kOffDO = 2 * kQTile;         // 2 stages
-  static constexpr int kOffL = 4 * kQTile;          // 2 stages x (LSE2[kBM], D[kBM]) fp32
-  static constexpr int kLdsBytes = kOffL + 2 * 2 * kBM * 4;
-  // dK^T / dV^T flush: [kBN][D] fp32 with a 16-byte row pad, over the Q/dO area
+  static constexpr int kQGroups = kBM / kG;           // groups of one step's Q (or dO)
+  static constexpr int kQTile = kQGroups * kGB;
+  static constexpr int kRing = 4;                     // steps held in LDS
+  static constexpr int kOffQ = 0;                     // kRing stages
+  static constexpr int kOffDO = kRing * kQTile;       // kRing stages
+  static constexpr int kLSlot = 512;                  // LSE[64] then D[64], fp32
+  static constexpr int kOffL = 2 * kRing * kQTile;    // kRing slots
+  static constexpr int kXPair = 4 * 64 * 16;          // P[2], dS[2] operands of one pair
+  static constexpr int kXBuf = kPairs * kXPair;
+  static constexpr int kOffX = kOffL + kRing * kLSlot;  // 2 buffers
+  static constexpr int kLdsBytes = kOffX + 2 * kXBuf;
+  // per wave and step: Q and dO groups spread over all waves, and one more
+  // load (LSE or D) on the last two waves
+  static constexpr int kLoadsPerWave = 2 * kQGroups / kWaves;
+  // dK^T / dV^T flush: [kBN][D] fp32 with a 16-byte row pad, over the Q/dO ring
   static constexpr int kFlushPitch = D * 4 + 16;
-  static_assert(kBN == kWaves * 32 && kBM % 32 == 0, "shapes");
-  static_assert(kBN * kFlushPitch <= kOffL, "flush buffer fits the Q/dO stages");
+  static_assert(kBN == kPairs * 32 && kBM == 32, "shapes");
+  static_assert((2 * kQGroups) % kWaves == 0, "loads spread evenly");
+  static_assert(kBN * kFlushPitch <= kOffL, "flush buffer fits the Q/dO ring");
 };
 
 // dq_kernel: the forward's tile shape and LDS layout, 64-key blocks.
@@ -303,193 +316,208 @@ __device__ __forceinline__ void dkdv_tile(const zl_tile& tile, const __bf16* __r
                                           float* __restrict__ dV, int H, float scale,
                                           char ZL_LDS* smem) {
   using C = Bwd<D>;
-  constexpr int DS = C::kDS, DB = C::kDB, QB = C::kQB, G = C::kG, GB = C::kGB;
+  constexpr int DS = C::kDS, DB = C::kDB, G = C::kG, GB = C::kGB;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wave < C::kPairs;  // waves w and w + 4 share SIMD w % 4
+  const int pair = producer ? wave : wave - C::kPairs;
   const int l32 = lane & 31;
   const int half = lane >> 5;
   const int64_t rs = int64_t(H) * D;
-  const float c = scale * kLog2e;
-
-  // ---- this lane's key: K^T / V^T operands (k = head_dim, j = key)
-  const int key = wave * 32 + l32;
-  const bool kvalid = key < tile.kv_len;
-  bf16x8 kf[DS], vf[DS];
-  {
-    const int64_t kr = tile.kv_row0 + (kvalid ? key : 0);
-    const __bf16* kp = K + kr * rs + int64_t(tile.head) * D + 8 * half;
-    const __bf16* vp = V + kr * rs + int64_t(tile.head) * D + 8 * half;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + ds * 16);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(vp + ds * 16);
-      kf[ds] = kvalid ? a : bf16x8{};
-      vf[ds] = kvalid ? b : bf16x8{};
-    }
-  }
-
-  // ---- direct-to-LDS loads of `nrows` rows starting at packed row `row0`;
-  // rows at or past `valid` read as zero. Lane l carries row l % G, chunk l / G
-  // of a 1 KB group; wave w fills groups w, w + 4, ...
-  const int ld_lane = (lane % G) * int(rs) * 2 + (lane / G) * 16;
-  auto issue_rows = [&](const __bf16* base, int64_t row0, int valid, int nrows, int lds_off)
-                        __attribute__((always_inline)) {
-    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(nrows, valid)));
-    const int64_t addr = uniform_i64(reinterpret_cast<int64_t>(base + row0 * rs + int64_t(tile.head) * D));
-    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<__bf16*>(addr), 0,
-                                                        rows * int(rs) * 2, kBufferFlags);
-    for (int gi = wave; gi < nrows / G; gi += C::kWaves)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void ZL_LDS*)(smem + lds_off + gi * GB), 16,
-                                               ld_lane,
-                                               __builtin_amdgcn_readfirstlane(gi * G * int(rs) * 2),
-                                               0, 0);
-  };
-  // LSE2 = LSE * log2 e (+inf past the item: P = 0) and D for a step, loaded
-  // into registers by threads 0..2*kBM-1 and stored to LDS later.
-  auto load_ld = [&](int step) __attribute__((always_inline)) {
-    float x = 0.f;
-    if (tid < 2 * C::kBM) {
-      const int r = step * C::kBM + (tid % C::kBM);
-      const int64_t idx = (tile.q_row0 + r) * H + tile.head;
-      if (r < tile.q_rows)
-        x = tid < C::kBM ? LSE[idx] * kLog2e : Dws[idx];
-      else
-        x = tid < C::kBM ? INFINITY : 0.f;
-    }
-    return x;
-  };
-  auto store_ld = [&](int stage, float x) __attribute__((always_inline)) {
-    if (tid < 2 * C::kBM)
-      *reinterpret_cast<float ZL_LDS*>(smem + C::kOffL + stage * 2 * C::kBM * 4 + tid * 4) = x;
-  };
-
-  // ---- per-lane LDS offsets
-  // row reads (A of S and dP): row qb*32 + l32, chunk 2*ds + half
-  const int a_lane = grp_off(l32, 8 * half, G, GB);
-  // transpose reads of Q^T / dO^T (A of dK^T / dV^T): rows in the order the
-  // S accumulator keeps them, 4*half + e and 8 + 4*half + e
-  const int e_l = (lane & 15) >> 2;
-  const int c_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int tq_lane = ((4 * half + e_l) / G) * GB + (c_l * G + (4 * half + e_l) % G) * 16 + (lane & 1) * 8;
-
-  auto tr8 = [&](const char ZL_LDS* p0, const char ZL_LDS* p1) __attribute__((always_inline)) {
-    const i16x4 lo = lds_read_tr16(p0);
-    const i16x4 hi = lds_read_tr16(p1);
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-  // Row r0 + 8 in a group layout is (8 / G) groups and (8 % G) rows further.
-  constexpr int kPlus8 = (8 / G) * GB + (8 % G) * 16;
-
-  f32x16 dk[DB], dv[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) {
-    dk[i] = f32x16{};
-    dv[i] = f32x16{};
-  }
-
   const int nsteps = (tile.q_rows + C::kBM - 1) / C::kBM;
-  // ---- prologue: step 0 of Q / dO / LSE / D
-  issue_rows(Q, tile.q_row0, tile.q_rows, C::kBM, C::kOffQ);
-  issue_rows(dO, tile.q_row0, tile.q_rows, C::kBM, C::kOffDO);
-  store_ld(0, load_ld(0));
-  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- direct-to-LDS loads of step `step`: Q and dO rows (rows at or past
+  // the item's end read as zero), and on waves 6 / 7 the LSE / D values
+  const int ld_lane = (lane % G) * int(rs) * 2 + (lane / G) * 16;
+  auto issue_step = [&](int step) __attribute__((always_inline)) {
+    const int slot = step % C::kRing;
+    const int valid = tile.q_rows - step * C::kBM;
+    const int64_t row0 = tile.q_row0 + int64_t(step) * C::kBM;
+#pragma unroll
+    for (int i = 0; i < C::kLoadsPerWave; ++i) {
+      const int gi = wave + i * C::kWaves;  // over [Q groups, dO groups]
+      const bool is_q = gi < C::kQGroups;
+      const int g = is_q ? gi : gi - C::kQGroups;
+      const __bf16* base = (is_q ? Q : dO) + row0 * rs + int64_t(tile.head) * D;
+      const int64_t addr = uniform_i64(reinterpret_cast<int64_t>(base));
+      const int rows = __builtin_amdgcn_readfirstlane(min(C::kBM, valid));
+      const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<__bf16*>(addr), 0,
+                                                          rows * int(rs) * 2, kBufferFlags);
+      const int off = (is_q ? C::kOffQ : C::kOffDO) + slot * C::kQTile + g * GB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void ZL_LDS*)(smem + off), 16, ld_lane,
+                                               __builtin_amdgcn_readfirstlane(g * G * int(rs) * 2),
+                                               0, 0);
+    }
+    if (wave >= C::kWaves - 2) {
+      const bool is_lse = wave == C::kWaves - 2;
+      const float* base = (is_lse ? LSE : Dws) + row0 * H + tile.head;
+      const int64_t addr = uniform_i64(reinterpret_cast<int64_t>(base));
+      const int rows = __builtin_amdgcn_readfirstlane(min(64, valid));
+      const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<float*>(addr), 0,
+                                                          rows * H * 4, kBufferFlags);
+      const int off = C::kOffL + slot * C::kLSlot + (is_lse ? 0 : 256);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void ZL_LDS*)(smem + off), 4, lane * H * 4,
+                                               0, 0, 0);
+    }
+  };
+  // wait until this wave's loads of earlier steps have landed; the loads
+  // issued in this iteration (if any) may still fly
+  auto wait_older = [&](bool issued) __attribute__((always_inline)) {
+    if (!issued)
+      __builtin_amdgcn_s_waitcnt(kWaitLoads);
+    else if (wave >= C::kWaves - 2)
+      __builtin_amdgcn_s_waitcnt(kWaitLoads + C::kLoadsPerWave + 1);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitLoads + C::kLoadsPerWave);
+  };
+
+  // exchange buffer: operand `kind` (0 = P, 1 = dS), half `u` of pair `pair`
+  auto xoff = [&](int step, int kind, int u) __attribute__((always_inline)) {
+    return C::kOffX + (step & 1) * C::kXBuf + pair * C::kXPair + (kind * 2 + u) * 1024 + lane * 16;
+  };
+
+  // prologue: steps 0 and 1
+  issue_step(0);
+  if (nsteps > 1) issue_step(1);
+  wait_older(nsteps > 1);
   __syncthreads();
 
-  const bool ragged_keys = tile.kv_len < C::kBN;
-  for (int step = 0; step < nsteps; ++step) {
-    const int st = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) {
-      const int64_t r1 = tile.q_row0 + int64_t(step + 1) * C::kBM;
-      const int v1 = tile.q_rows - (step + 1) * C::kBM;
-      issue_rows(Q, r1, v1, C::kBM, C::kOffQ + (st ^ 1) * C::kQTile);
-      issue_rows(dO, r1, v1, C::kBM, C::kOffDO + (st ^ 1) * C::kQTile);
-    }
-    // issued after the direct loads: waiting for it waits for them too
-    const float ld_next = more ? load_ld(step + 1) : 0.f;
-
-    const char ZL_LDS* qs = smem + C::kOffQ + st * C::kQTile;
-    const char ZL_LDS* gs = smem + C::kOffDO + st * C::kQTile;
-    const char ZL_LDS* ls = smem + C::kOffL + st * 2 * C::kBM * 4;
-
-    // ---- S = Q K^T and dP = dO V^T (lane = key, registers = queries)
-    f32x16 s[QB], dp[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      s[qb] = f32x16{};
-      dp[qb] = f32x16{};
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const int off = (qb * 32 / G) * GB + a_lane + ds * 2 * G * 16;
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(qs + off), kf[ds], s[qb], 0, 0, 0);
-        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(gs + off), vf[ds], dp[qb], 0, 0, 0);
-      }
-    }
-
-    // ---- P and dS; register r holds query qb*32 + 8*(r/4) + 4*half + r%4
-    bf16x8 pf[QB][2], sf[QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qo = (qb * 32 + 8 * g + 4 * half) * 4;
-        const f32x4 l2 = *reinterpret_cast<const f32x4 ZL_LDS*>(ls + qo);
-        const f32x4 dd = *reinterpret_cast<const f32x4 ZL_LDS*>(ls + C::kBM * 4 + qo);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -l2[e]));
-          if (ragged_keys && !kvalid) p = 0.f;
-          const float dsv = scale * p * (dp[qb][r] - dd[e]);
-          pf[qb][r >> 3][r & 7] = (__bf16)p;
-          sf[qb][r >> 3][r & 7] = (__bf16)dsv;
-        }
-      }
-    }
-
-    // ---- dV^T += dO^T P, dK^T += Q^T dS; k-slot e of operand (qb, u) in
-    // half h is query qb*32 + 16u + 8(e/4) + 4h + e%4 (the S register order)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int off = ((qb * 32 + 16 * u) / G) * GB + tq_lane + db * 4 * G * 16;
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr8(gs + off, gs + off + kPlus8), pf[qb][u],
-                                                           dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr8(qs + off, qs + off + kPlus8), sf[qb][u],
-                                                           dk[db], 0, 0, 0);
-        }
-
-    // the next step's direct loads were issued at the top of this step
-    __builtin_amdgcn_s_waitcnt(kWaitLoads);
-    if (more) store_ld(st ^ 1, ld_next);
-    __syncthreads();
-  }
-
-  // ---- dK, dV: registers -> LDS [key][d] fp32 -> coalesced atomics
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  auto flush = [&](const f32x16 (&acc)[DB], float* __restrict__ out) __attribute__((always_inline)) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 x = {acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
-        *reinterpret_cast<f32x4 ZL_LDS*>(smem + key * C::kFlushPitch + (db * 32 + 8 * g + 4 * half) * 4) = x;
-      }
-    __syncthreads();
+  const int key = pair * 32 + l32;
+  const bool kvalid = key < tile.kv_len;
+  // flush of one of dK / dV staged in LDS as [key][d] fp32 by the consumers:
+  // every thread adds a strided share with coalesced fp32 atomics
+  auto add_staged = [&](float* __restrict__ out) __attribute__((always_inline)) {
     for (int idx = tid; idx < tile.kv_len * D; idx += C::kThreads) {
       const int kr = idx / D, col = idx % D;
       const float x = *reinterpret_cast<const float ZL_LDS*>(smem + kr * C::kFlushPitch + col * 4);
       atomicAdd(out + ((tile.kv_row0 + kr) * H + tile.head) * D + col, x);
     }
-    __syncthreads();
   };
-  flush(dk, dK);
-  flush(dv, dV);
+  if (producer) {
+    // ---- K / V rows of this lane's key (k = head_dim, j = key)
+    bf16x8 kf[DS], vf[DS];
+    {
+      const int64_t kr = tile.kv_row0 + (kvalid ? key : 0);
+      const int64_t off = kr * rs + int64_t(tile.head) * D + 8 * half;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(K + off + ds * 16);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(V + off + ds * 16);
+        kf[ds] = kvalid ? a : bf16x8{};
+        vf[ds] = kvalid ? b : bf16x8{};
+      }
+    }
+    const float c = scale * kLog2e;
+    const bool ragged_keys = tile.kv_len < C::kBN;
+    // row reads (A of S and dP): row l32, chunk 2*ds + half
+    const int a_lane = (l32 / G) * GB + (half * G + l32 % G) * 16;
+    for (int j = 0; j <= nsteps; ++j) {
+      const bool issue = j + 2 < nsteps;
+      if (issue) issue_step(j + 2);
+      if (j < nsteps) {
+        const int slot = j % C::kRing;
+        int qa = C::kOffQ + slot * C::kQTile + a_lane;
+        int ga = C::kOffDO + slot * C::kQTile + a_lane;
+        asm volatile("" : "+v"(qa), "+v"(ga));
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(smem + qa + ds * 2 * G * 16), kf[ds], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(smem + ga + ds * 2 * G * 16), vf[ds], dp, 0, 0, 0);
+        }
+        // register r holds query 8*(r/4) + 4*half + r%4
+        const char ZL_LDS* ls = smem + C::kOffL + slot * C::kLSlot;
+        bf16x8 pf[2], sf[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 lse = *reinterpret_cast<const f32x4 ZL_LDS*>(ls + (8 * g + 4 * half) * 4);
+          const f32x4 dd = *reinterpret_cast<const f32x4 ZL_LDS*>(ls + 256 + (8 * g + 4 * half) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse[e] * kLog2e));
+            if (ragged_keys && !kvalid) p = 0.f;
+            pf[r >> 3][r & 7] = (__bf16)p;
+            sf[r >> 3][r & 7] = (__bf16)((dp[r] - dd[e]) * (p * scale));
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          *reinterpret_cast<bf16x8 ZL_LDS*>(smem + xoff(j, 0, u)) = pf[u];
+          *reinterpret_cast<bf16x8 ZL_LDS*>(smem + xoff(j, 1, u)) = sf[u];
+        }
+      }
+      wait_older(issue);
+      __syncthreads();
+    }
+    // the consumers stage dK, then dV
+#pragma unroll
+    for (int kind = 0; kind < 2; ++kind) {
+      __syncthreads();
+      add_staged(kind == 0 ? dK : dV);
+      __syncthreads();
+    }
+  } else {
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) {
+      dk[i] = f32x16{};
+      dv[i] = f32x16{};
+    }
+    // transpose reads of Q^T / dO^T (A of dK^T / dV^T): rows in the order the
+    // producer's S accumulator keeps them, 4*half + e and 8 + 4*half + e
+    const int e_l = (lane & 15) >> 2;
+    const int c_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int tq_lane = ((4 * half + e_l) / G) * GB + (c_l * G + (4 * half + e_l) % G) * 16 + (lane & 1) * 8;
+    constexpr int kPlus8 = (8 / G) * GB + (8 % G) * 16;  // 8 rows further
+    auto tr8 = [&](int a) __attribute__((always_inline)) {
+      const i16x4 lo = lds_read_tr16(smem + a);
+      const i16x4 hi = lds_read_tr16(smem + a + kPlus8);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    for (int j = 0; j <= nsteps; ++j) {
+      const bool issue = j + 2 < nsteps;
+      if (issue) issue_step(j + 2);
+      if (j > 0) {
+        const int st = j - 1;  // the producer wrote this step last iteration
+        const int slot = st % C::kRing;
+        int qa = C::kOffQ + slot * C::kQTile + tq_lane;
+        int ga = C::kOffDO + slot * C::kQTile + tq_lane;
+        asm volatile("" : "+v"(qa), "+v"(ga));
+        // k-slot e of operand u in half h is query 16u + 8(e/4) + 4h + e%4
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 pf = *reinterpret_cast<const bf16x8 ZL_LDS*>(smem + xoff(st, 0, u));
+          const bf16x8 sf = *reinterpret_cast<const bf16x8 ZL_LDS*>(smem + xoff(st, 1, u));
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int off = ((16 * u) / G) * GB + db * 4 * G * 16;
+            dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr8(ga + off), pf, dv[db], 0, 0, 0);
+            dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr8(qa + off), sf, dk[db], 0, 0, 0);
+          }
+        }
+      }
+      wait_older(issue);
+      __syncthreads();
+    }
+    // ---- dK^T then dV^T -> LDS [key][d] fp32 (over the Q/dO ring, no longer
+    // read; register r of block db is d = db*32 + 8(r/4) + 4*half + r%4)
+#pragma unroll
+    for (int kind = 0; kind < 2; ++kind) {
+      const f32x16 (&acc)[DB] = kind == 0 ? dk : dv;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 x = {acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+          *reinterpret_cast<f32x4 ZL_LDS*>(smem + key * C::kFlushPitch + (db * 32 + 8 * g + 4 * half) * 4) = x;
+        }
+      __syncthreads();
+      add_staged(kind == 0 ? dK : dV);
+      __syncthreads();
+    }
+  }
 }
 
 template <int D>

@@ -22,10 +22,11 @@ constexpr int kFwdWaves = ZL_FWD_WAVES;
 constexpr int kFwdBlockM = kFwdWaves * 32;
 constexpr int kFwdBlockN = ZL_FWD_BLOCK_N;
 static_assert(kFwdBlockM == 256, "the worklist cuts 256-row tiles");
-// Backward tile: 4 waves x 32 keys, streaming 64 query rows per step.
-constexpr int kBwdWaves = 4;
-constexpr int kBwdBlockN = kBwdWaves * 32;
-constexpr int kBwdBlockM = 64;
+// dK/dV backward tile: 4 producer / consumer wave pairs x 32 keys, streaming
+// 32 query rows per step.
+constexpr int kBwdPairs = 4;
+constexpr int kBwdBlockN = kBwdPairs * 32;
+constexpr int kBwdBlockM = 32;
 
 // Per-tile fixed cost in (query row x key) units used by the LPT rule: the
 // prologue and epilogue of a tile cost about as much as 64 keys of work.
