@@ -214,7 +214,7 @@ __device__ __forceinline__ void dq_tile(const zl_tile& tile, const __bf16* __res
   for (int j = 0; j < nblk; ++j) {
     // K(j), V(j) are older than the two loads of block j + 1
     __builtin_amdgcn_s_waitcnt(kWaitLoads + 2 * kLoadsPerTile);
-    __syncthreads();  // every wave's part of block j has landed; block j - 1 is no longer read
+    lds_barrier();  // every wave's part of block j has landed; block j - 1 is no longer read
     issue_tile(kbase, kstage(j + 2), j + 2);
     issue_tile(vbase, vstage(j + 2), j + 2);
     const char ZL_LDS* kr = opaque(kstage(j) + r_lane);
@@ -449,7 +449,7 @@ __device__ __forceinline__ void dkdv_tile(const zl_tile& tile, const __bf16* __r
         }
       }
       wait_older(issue);
-      __syncthreads();
+      lds_barrier();
     }
     // the consumers stage dK, then dV
 #pragma unroll
@@ -499,7 +499,7 @@ __device__ __forceinline__ void dkdv_tile(const zl_tile& tile, const __bf16* __r
         }
       }
       wait_older(issue);
-      __syncthreads();
+      lds_barrier();
     }
     // ---- dK^T then dV^T -> LDS [key][d] fp32 (over the Q/dO ring, no longer
     // read; register r of block db is d = db*32 + 8(r/4) + 4*half + r%4)

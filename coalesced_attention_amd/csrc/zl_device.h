@@ -41,6 +41,18 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Workgroup barrier for the LDS hand-offs inside pipelined loops.
+// __syncthreads() carries a workgroup-scope fence, for which the compiler
+// drains every outstanding vector-memory operation -- including direct-to-LDS
+// prefetches meant for later iterations. This barrier waits only for this
+// wave's own LDS reads and writes (lgkmcnt 0) and then meets the other waves;
+// a wave waits for the direct loads the next iteration needs with an explicit
+// vmcnt before it. The "memory" clobber keeps the compiler from moving any
+// memory access across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // An empty asm that reads `x`: x must be computed before this point.
 template <typename T>
 __device__ __forceinline__ void pin(const T& x) {
