@@ -105,29 +105,38 @@ def _cpu_baseline(wl, inp, target_s):
     Qh, Kh, Vh = (x.float().numpy() for x in (inp.q, inp.k, inp.v))
     s = wl.softmax_scale
     d = wl.head_dim
-    # round-robin over (item, head) units: sampled rows of long items, all
-    # rows of short ones; stop once the target time is spent
-    units = []
-    for idx, it in enumerate(wl.items):
-        rows = sample_rows(it, seed=idx)
-        for h in range(it.head_begin, it.head_begin + it.head_cnt):
-            units.append((it, h, rows))
-    order = np.random.default_rng(0).permutation(len(units))
+    # pass 0: the rows the parity tests check (every row of short items,
+    # four per 128-row block of long ones), in a seeded random order of
+    # (item, head) units; later passes: fresh seeded rows of the long items;
+    # stop once the target time is spent
+    def units_of(pass_no):
+        out = []
+        for idx, it in enumerate(wl.items):
+            if pass_no > 0 and it.q_len <= 1024:
+                continue
+            rows = sample_rows(it, seed=idx + 1000 * pass_no)
+            for h in range(it.head_begin, it.head_begin + it.head_cnt):
+                out.append((it, h, rows))
+        return [out[i] for i in np.random.default_rng(pass_no).permutation(len(out))]
     flops = 0
     rows_done = 0
+    passes = 0
     t0 = time.perf_counter()
-    for u in order:
-        it, h, rows = units[u]
-        coalesced_forward_rows(Qh, Kh, Vh, it, h, rows, s)
-        flops += 4 * len(rows) * it.kv_len * d
-        rows_done += len(rows)
-        if time.perf_counter() - t0 > target_s:
-            break
+    while time.perf_counter() - t0 <= target_s:
+        for it, h, rows in units_of(passes):
+            coalesced_forward_rows(Qh, Kh, Vh, it, h, rows, s)
+            flops += 4 * len(rows) * it.kv_len * d
+            rows_done += len(rows)
+            if time.perf_counter() - t0 > target_s:
+                break
+        passes += 1
     el = time.perf_counter() - t0
     total_rows = sum(it.q_len * it.head_cnt for it in wl.items)
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows_done} of {total_rows} (query row, head) pairs of the same workload "
-                      f"({flops / 1e9:.1f} GFLOP in {el:.1f} s, fp64 numpy)"}
+            "sample": f"{rows_done} (query row, head) pairs of the same workload ({total_rows} in all): "
+                      f"every image row and 4 rows per 128-row block of the video shard, then "
+                      f"fresh rows of the shard ({passes} pass(es); {flops / 1e9:.1f} GFLOP in "
+                      f"{el:.1f} s, fp64 numpy)"}
 
 
 def _bench_backward(zl, W, dev, stream, n_slots):
