@@ -40,6 +40,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload index (2 = mixed rank share)")
     ap.add_argument("--n-slots", type=int, default=-1, help="static slots (-1: one per CU, 0: one WG per tile)")
+    ap.add_argument("--kv-chunk", type=int, default=0,
+                    help="split items with more keys into key chunks merged inside the forward (0: off)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
@@ -208,15 +210,17 @@ def main():
 
     t0 = time.perf_counter()
     built = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim,
-                              n_slots=n_slots)
+                              n_slots=n_slots, kv_chunk=a.kv_chunk)
     wl_ms = (time.perf_counter() - t0) * 1e3
     built.to(dev)
     o = torch.empty((wl.q_rows, wl.num_heads, wl.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((wl.q_rows, wl.num_heads), dtype=torch.float32, device=dev)
+    ws = (torch.empty(built.workspace_floats, dtype=torch.float32, device=dev)
+          if built.workspace_floats else None)
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        zl.coalesced_attn_fwd(built, q, k, v, o, lse, stream=stream)
+        zl.coalesced_attn_fwd(built, q, k, v, o, lse, stream=stream, workspace=ws)
 
     for _ in range(a.warmup):
         step()
@@ -236,7 +240,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "items": len(wl.items), "q_rows": wl.q_rows,
                    "kv_rows": wl.kv_rows, "heads": wl.num_heads, "head_dim": wl.head_dim,
-                   "tiles": built.n_tiles, "n_slots": n_slots, "flops_per_step": flops},
+                   "tiles": built.n_tiles, "n_slots": n_slots, "flops_per_step": flops,
+                   "kv_chunk": a.kv_chunk,
+                   "schedule_makespan_over_mean": round(built.header.max_slot_cost * max(1, n_slots)
+                                                        / max(1, built.header.total_cost), 4)},
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

@@ -559,12 +559,13 @@ int launch_bwd(const zl_worklist_header* h, const char* d_wl, const void* q, con
   const __bf16* K = static_cast<const __bf16*>(k);
   const __bf16* V = static_cast<const __bf16*>(v);
   const __bf16* G = static_cast<const __bf16*>(dout);
-  // dQ and D over the forward's tiles and slots, then dK / dV (which read D)
-  const int qgrid = h->n_slots > 0 ? h->n_slots : h->n_tiles;
-  if (qgrid > 0 && h->n_tiles > 0) {
+  // dQ and D over the unsplit forward tiles and slots, then dK / dV (which
+  // read D)
+  const int qgrid = h->n_slots > 0 ? h->n_slots : h->n_dq_tiles;
+  if (qgrid > 0 && h->n_dq_tiles > 0) {
     hipLaunchKernelGGL(dq_kernel<D>, dim3(qgrid), dim3(BwdQ<D>::kThreads), 0, stream,
-                       reinterpret_cast<const zl_tile*>(d_wl + h->tiles_offset),
-                       reinterpret_cast<const int32_t*>(d_wl + h->slots_offset), h->n_slots, Q, K,
+                       reinterpret_cast<const zl_tile*>(d_wl + h->dq_tiles_offset),
+                       reinterpret_cast<const int32_t*>(d_wl + h->dq_slots_offset), h->n_slots, Q, K,
                        V, G, o, lse, d_ws, dq, h->num_heads, h->softmax_scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return zl::fail(ZL_ERR_HIP, "backward dQ launch: %s", hipGetErrorString(e));

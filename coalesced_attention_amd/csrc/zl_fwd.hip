@@ -71,12 +71,14 @@ struct Fwd {
   static_assert(kBN % 32 == 0 && (D == 64 || D == 128), "shapes");
 };
 
+// O / LSE rows of the tile start at out_row0 (q_row0, or a workspace row for
+// a key chunk of a split item).
 template <int D>
 __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __restrict__ Q,
                                          const __bf16* __restrict__ K,
                                          const __bf16* __restrict__ V, float* __restrict__ O,
-                                         float* __restrict__ LSE, int H, float c,
-                                         char ZL_LDS* smem) {
+                                         float* __restrict__ LSE, int64_t out_row0, int H,
+                                         float c, char ZL_LDS* smem) {
   using C = Fwd<D>;
   constexpr int KB = C::kKB, DS = C::kDS, DB = C::kDB, G = C::kG, GB = C::kGroupBytes;
   const int tid = threadIdx.x;
@@ -315,7 +317,7 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? kLn2 * (m_use + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
   if (qvalid) {
-    float* op = O + (tile.q_row0 + qr) * rs + int64_t(tile.head) * D + 4 * half;
+    float* op = O + (out_row0 + qr) * rs + int64_t(tile.head) * D + 4 * half;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -324,15 +326,17 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
         f32x4 x = {a[4 * g] * inv, a[4 * g + 1] * inv, a[4 * g + 2] * inv, a[4 * g + 3] * inv};
         *reinterpret_cast<f32x4*>(op + db * 32 + 8 * g) = x;
       }
-    if (half == 0) LSE[(tile.q_row0 + qr) * H + tile.head] = lse;
+    if (half == 0) LSE[(out_row0 + qr) * H + tile.head] = lse;
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(Fwd<D>::kThreads, 1) void fwd_kernel(
     const zl_tile* __restrict__ tiles, const int32_t* __restrict__ slots, int n_slots,
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, int H, float c) {
+    const zl_outmap* __restrict__ outmap, const __bf16* __restrict__ Q,
+    const __bf16* __restrict__ K, const __bf16* __restrict__ V, float* __restrict__ O,
+    float* __restrict__ LSE, float* __restrict__ ws_o, float* __restrict__ ws_lse, int H,
+    float c) {
   __shared__ __attribute__((aligned(16))) char smem_raw[Fwd<D>::kLdsBytes];
   char ZL_LDS* smem = (char ZL_LDS*)(smem_raw);  // generic -> LDS address space
   int t0, t1;
@@ -353,24 +357,32 @@ __global__ __launch_bounds__(Fwd<D>::kThreads, 1) void fwd_kernel(
   t1 = __builtin_amdgcn_readfirstlane(t1);
   for (int t = t0; t < t1; ++t) {
     const zl_tile tile = uniform_tile(tiles[t]);
-    run_tile<D>(tile, Q, K, V, O, LSE, H, c, smem);
+    const zl_outmap om = outmap[tile.item];
+    const bool to_ws = __builtin_amdgcn_readfirstlane(om.to_workspace) != 0;
+    const int64_t out_row0 = tile.q_row0 + uniform_i64(om.o_shift);
+    run_tile<D>(tile, Q, K, V, to_ws ? ws_o : O, to_ws ? ws_lse : LSE, out_row0, H, c, smem);
     __syncthreads();  // LDS is reused by the next tile
   }
 }
 
 template <int D>
 int launch_fwd(const zl_worklist_header* h, const char* d_wl, const void* q, const void* k,
-               const void* v, float* o, float* lse, hipStream_t stream) {
+               const void* v, float* o, float* lse, float* ws, hipStream_t stream) {
   const int grid = h->n_slots > 0 ? h->n_slots : h->n_tiles;
   if (grid == 0 || h->n_tiles == 0) return ZL_OK;
   const float c = h->softmax_scale * kLog2e;
+  float* ws_o = ws;
+  float* ws_lse = ws ? ws + h->ws_rows * int64_t(h->num_heads) * D : nullptr;
   hipLaunchKernelGGL(fwd_kernel<D>, dim3(grid), dim3(Fwd<D>::kThreads), 0, stream,
                      reinterpret_cast<const zl_tile*>(d_wl + h->tiles_offset),
                      reinterpret_cast<const int32_t*>(d_wl + h->slots_offset), h->n_slots,
+                     reinterpret_cast<const zl_outmap*>(d_wl + h->outmap_offset),
                      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), o, lse, h->num_heads, c);
+                     static_cast<const __bf16*>(v), o, lse, ws_o, ws_lse, h->num_heads, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return zl::fail(ZL_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  if (h->n_merges > 0)
+    return zl::launch_merge_list(h, d_wl, ws_o, ws_lse, o, lse, stream);
   return ZL_OK;
 }
 
@@ -378,18 +390,21 @@ int launch_fwd(const zl_worklist_header* h, const char* d_wl, const void* q, con
 
 extern "C" int zl_coalesced_attn_fwd(const void* h_wl, const void* d_wl, const void* q,
                                      const void* k, const void* v, float* o, float* lse,
-                                     void* stream) {
+                                     float* workspace, void* stream) {
   zl::clear_error();
   const zl_worklist_header* h = nullptr;
   int rc = zl::check_worklist(h_wl, &h);
   if (rc) return rc;
   if (!d_wl || !q || !k || !v || !o || !lse)
     return zl::fail(ZL_ERR_NULL, "device pointers must be non-NULL");
+  if (h->ws_rows > 0 && !workspace)
+    return zl::fail(ZL_ERR_NULL, "the worklist splits items: workspace must be non-NULL");
   if (!zl::aligned16(d_wl) || !zl::aligned16(q) || !zl::aligned16(k) || !zl::aligned16(v) ||
-      !zl::aligned16(o) || !zl::aligned16(lse))
+      !zl::aligned16(o) || !zl::aligned16(lse) || (h->ws_rows > 0 && !zl::aligned16(workspace)))
     return zl::fail(ZL_ERR_ALIGN, "device pointers must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const char* dw = static_cast<const char*>(d_wl);
-  return h->head_dim == 128 ? launch_fwd<128>(h, dw, q, k, v, o, lse, s)
-                            : launch_fwd<64>(h, dw, q, k, v, o, lse, s);
+  float* ws = h->ws_rows > 0 ? workspace : nullptr;
+  return h->head_dim == 128 ? launch_fwd<128>(h, dw, q, k, v, o, lse, ws, s)
+                            : launch_fwd<64>(h, dw, q, k, v, o, lse, ws, s);
 }

@@ -64,9 +64,29 @@ int check_worklist(const void* h_wl, const zl_worklist_header** hdr) {
     if (h->bwd_slots_offset < need) return fail(ZL_ERR_WORKLIST, "worklist sections overlap");
     need = h->bwd_slots_offset + uint64_t(h->n_slots + 1) * sizeof(int32_t);
   }
+  if (h->kv_chunk < 0 || h->n_vitems < h->n_items || h->n_merges < 0 || h->n_dq_tiles < 0 ||
+      h->ws_rows < 0 || (h->n_merges > 0) != (h->ws_rows > 0))
+    return fail(ZL_ERR_WORKLIST, "worklist split fields out of range");
+  if (h->outmap_offset < need) return fail(ZL_ERR_WORKLIST, "worklist sections overlap");
+  need = h->outmap_offset + uint64_t(h->n_vitems) * sizeof(zl_outmap);
+  if (h->merges_offset < need) return fail(ZL_ERR_WORKLIST, "worklist sections overlap");
+  need = h->merges_offset + uint64_t(h->n_merges) * sizeof(zl_merge);
+  if (h->n_merges == 0) {
+    if (h->dq_tiles_offset != h->tiles_offset || h->dq_slots_offset != h->slots_offset ||
+        h->n_dq_tiles != h->n_tiles)
+      return fail(ZL_ERR_WORKLIST, "worklist dQ section must alias the forward one");
+  } else {
+    if (h->dq_tiles_offset < need) return fail(ZL_ERR_WORKLIST, "worklist sections overlap");
+    need = h->dq_tiles_offset + uint64_t(h->n_dq_tiles) * sizeof(zl_tile);
+    if (h->n_slots > 0) {
+      if (h->dq_slots_offset < need) return fail(ZL_ERR_WORKLIST, "worklist sections overlap");
+      need = h->dq_slots_offset + uint64_t(h->n_slots + 1) * sizeof(int32_t);
+    }
+  }
   if (h->tiles_offset < sizeof(zl_worklist_header) || (h->tiles_offset & 15u) ||
       (h->slots_offset & 15u) || (h->bwd_tiles_offset & 15u) || (h->bwd_slots_offset & 15u) ||
-      need > h->total_bytes)
+      (h->outmap_offset & 15u) || (h->merges_offset & 15u) || (h->dq_tiles_offset & 15u) ||
+      (h->dq_slots_offset & 15u) || need > h->total_bytes)
     return fail(ZL_ERR_WORKLIST, "worklist offsets inconsistent with its size");
   *hdr = h;
   return ZL_OK;
@@ -207,17 +227,40 @@ extern "C" int zl_build_worklist(const zl_problem* problem, const zl_item* items
   if ((p.head_dim != 64 && p.head_dim != 128) || p.num_heads < 1 || p.q_rows < 0 ||
       p.kv_rows < 0)
     return fail(ZL_ERR_SHAPE, "head_dim must be 64 or 128 and sizes non-negative");
-  if (p.reserved != 0) return fail(ZL_ERR_ARG, "problem.reserved must be 0");
+  if (p.kv_chunk < 0) return fail(ZL_ERR_ARG, "problem.kv_chunk must be >= 0");
   if (!(p.softmax_scale <= 0.f || std::isfinite(p.softmax_scale)))
     return fail(ZL_ERR_ARG, "softmax_scale must be finite");
   int rc = validate_items(p, items, n_items);
   if (rc) return rc;
 
   const int block_m = kFwdBlockM;
-  int64_t n_tiles64 = 0;
+  // Key split: item i has parts[i] chunks of chunk[i] keys (the last one
+  // shorter); only items with queries, heads and more than kv_chunk keys.
+  std::vector<int32_t> parts, chunk;
+  try {
+    parts.assign(size_t(n_items), 1);
+    chunk.assign(size_t(n_items), 0);
+  } catch (const std::bad_alloc&) {
+    return fail(ZL_ERR_ARG, "out of host memory for %d items", n_items);
+  }
+  int64_t n_unsplit64 = 0, n_tiles64 = 0, n_vitems64 = n_items, ws_rows = 0;
+  int32_t n_merges = 0;
   for (int32_t i = 0; i < n_items; ++i) {
     const zl_item& it = items[i];
-    n_tiles64 += int64_t(it.head_cnt) * ((int64_t(it.q_len) + block_m - 1) / block_m);
+    const int64_t qblocks = (int64_t(it.q_len) + block_m - 1) / block_m;
+    n_unsplit64 += int64_t(it.head_cnt) * qblocks;
+    if (p.kv_chunk > 0 && it.q_len > 0 && it.head_cnt > 0 && it.kv_len > p.kv_chunk) {
+      const int64_t n = (int64_t(it.kv_len) + p.kv_chunk - 1) / p.kv_chunk;
+      const int64_t c = ((int64_t(it.kv_len) + n - 1) / n + 63) / 64 * 64;
+      parts[size_t(i)] = int32_t((it.kv_len + c - 1) / c);
+      chunk[size_t(i)] = int32_t(c);
+    }
+    if (parts[size_t(i)] > 1) {
+      n_vitems64 += parts[size_t(i)];
+      ws_rows += int64_t(parts[size_t(i)]) * it.q_len;
+      ++n_merges;
+    }
+    n_tiles64 += int64_t(it.head_cnt) * qblocks * parts[size_t(i)];
   }
   int64_t n_bwd64 = 0;
   for (int32_t i = 0; i < n_items; ++i) {
@@ -225,14 +268,27 @@ extern "C" int zl_build_worklist(const zl_problem* problem, const zl_item* items
     if (it.q_len > 0)
       n_bwd64 += int64_t(it.head_cnt) * ((int64_t(it.kv_len) + kBwdBlockN - 1) / kBwdBlockN);
   }
-  if (n_tiles64 > INT32_MAX || n_bwd64 > INT32_MAX) return fail(ZL_ERR_ARG, "too many tiles");
+  if (n_tiles64 > INT32_MAX || n_bwd64 > INT32_MAX || n_vitems64 > INT32_MAX)
+    return fail(ZL_ERR_ARG, "too many tiles");
   const int32_t n_tiles = int32_t(n_tiles64), n_bwd_tiles = int32_t(n_bwd64);
+  const int32_t n_unsplit = int32_t(n_unsplit64), n_vitems = int32_t(n_vitems64);
+  const bool split = n_merges > 0;
   const uint64_t slot_bytes = n_slots > 0 ? uint64_t(n_slots + 1) * 4 : 0;
   const uint64_t tiles_off = align_up(sizeof(zl_worklist_header), 256);
   const uint64_t slots_off = align_up(tiles_off + uint64_t(n_tiles) * sizeof(zl_tile), 256);
   const uint64_t bwd_tiles_off = align_up(slots_off + slot_bytes, 256);
   const uint64_t bwd_slots_off = align_up(bwd_tiles_off + uint64_t(n_bwd_tiles) * sizeof(zl_tile), 256);
-  const uint64_t total = align_up(bwd_slots_off + slot_bytes, 256);
+  const uint64_t outmap_off = align_up(bwd_slots_off + slot_bytes, 256);
+  const uint64_t merges_off = align_up(outmap_off + uint64_t(n_vitems) * sizeof(zl_outmap), 256);
+  uint64_t end = align_up(merges_off + uint64_t(n_merges) * sizeof(zl_merge), 256);
+  uint64_t dq_tiles_off = tiles_off, dq_slots_off = n_slots > 0 ? slots_off : 0;
+  if (split) {
+    dq_tiles_off = end;
+    dq_slots_off = align_up(dq_tiles_off + uint64_t(n_unsplit) * sizeof(zl_tile), 256);
+    end = align_up(dq_slots_off + slot_bytes, 256);
+    if (n_slots == 0) dq_slots_off = 0;
+  }
+  const uint64_t total = end;
   if (!host_buf) {
     *bytes = size_t(total);
     return ZL_OK;
@@ -244,19 +300,45 @@ extern "C" int zl_build_worklist(const zl_problem* problem, const zl_item* items
   std::memset(base, 0, size_t(total));
   auto* hdr = reinterpret_cast<zl_worklist_header*>(base);
 
-  // Forward tiles: block_m query rows x one head x the item's key range.
+  // Forward tiles: block_m query rows x one head x the item's key range --
+  // the unsplit items first, in (item, head, query block) order, then the
+  // key chunks of split items as items n_items, n_items + 1, ... in (item,
+  // chunk, head, query block) order. The dQ pass uses the unsplit cut.
   const int64_t c0 = int64_t(block_m) * kCostC0PerRow;
-  std::vector<TileKey> tiles;
+  auto* outmap = reinterpret_cast<zl_outmap*>(base + outmap_off);
+  auto* merges = reinterpret_cast<zl_merge*>(base + merges_off);
+  std::vector<TileKey> tiles, dq_tiles;
   try {
     tiles.reserve(size_t(n_tiles));
-    for (int32_t i = 0; i < n_items; ++i) {
+    auto cut = [&](std::vector<TileKey>& out, int32_t i, int32_t vitem, int32_t k0, int32_t keys) {
       const zl_item& it = items[i];
       for (int32_t h = it.head_begin; h < it.head_begin + it.head_cnt; ++h)
         for (int32_t r0 = 0; r0 < it.q_len; r0 += block_m) {
           const int32_t rows = std::min(block_m, it.q_len - r0);
-          tiles.push_back(TileKey{zl_tile{it.q_off + r0, it.kv_off, rows, it.kv_len, h, i},
-                                  int64_t(rows) * it.kv_len + c0});
+          out.push_back(TileKey{zl_tile{it.q_off + r0, it.kv_off + k0, rows, keys, h, vitem},
+                                int64_t(rows) * keys + c0});
         }
+    };
+    for (int32_t i = 0; i < n_items; ++i) {
+      outmap[i] = zl_outmap{0, 0, 0};
+      if (parts[size_t(i)] == 1) cut(tiles, i, i, 0, items[i].kv_len);
+    }
+    int32_t vitem = n_items, m = 0;
+    int64_t ws_row = 0;
+    for (int32_t i = 0; i < n_items; ++i) {
+      if (parts[size_t(i)] == 1) continue;
+      const zl_item& it = items[i];
+      merges[m++] = zl_merge{it.q_off, ws_row, it.q_len, it.head_begin, it.head_cnt, parts[size_t(i)]};
+      for (int32_t pidx = 0; pidx < parts[size_t(i)]; ++pidx, ++vitem) {
+        const int32_t k0 = pidx * chunk[size_t(i)];
+        outmap[vitem] = zl_outmap{ws_row + int64_t(pidx) * it.q_len - it.q_off, 1, 0};
+        cut(tiles, i, vitem, k0, std::min(chunk[size_t(i)], it.kv_len - k0));
+      }
+      ws_row += int64_t(parts[size_t(i)]) * it.q_len;
+    }
+    if (split) {
+      dq_tiles.reserve(size_t(n_unsplit));
+      for (int32_t i = 0; i < n_items; ++i) cut(dq_tiles, i, i, 0, items[i].kv_len);
     }
   } catch (const std::bad_alloc&) {
     return fail(ZL_ERR_ARG, "out of host memory for %d tiles", n_tiles);
@@ -265,6 +347,13 @@ extern "C" int zl_build_worklist(const zl_problem* problem, const zl_item* items
   rc = schedule(tiles, n_slots, reinterpret_cast<zl_tile*>(base + tiles_off),
                 reinterpret_cast<int32_t*>(base + slots_off), &total_cost, &makespan);
   if (rc) return rc;
+  if (split) {
+    int64_t dq_total = 0, dq_makespan = 0;
+    rc = schedule(dq_tiles, n_slots, reinterpret_cast<zl_tile*>(base + dq_tiles_off),
+                  reinterpret_cast<int32_t*>(base + (n_slots > 0 ? dq_slots_off : dq_tiles_off)),
+                  &dq_total, &dq_makespan);
+    if (rc) return rc;
+  }
 
   // Backward tiles: block_n_bwd keys x one head x all of the item's queries.
   const int64_t c0_bwd = int64_t(kBwdBlockN) * kCostC0PerRow;
@@ -312,6 +401,15 @@ extern "C" int zl_build_worklist(const zl_problem* problem, const zl_item* items
   hdr->bwd_tiles_offset = bwd_tiles_off;
   hdr->bwd_slots_offset = n_slots > 0 ? bwd_slots_off : 0;
   hdr->bwd_max_slot_cost = bwd_makespan;
+  hdr->kv_chunk = p.kv_chunk;
+  hdr->n_vitems = n_vitems;
+  hdr->outmap_offset = outmap_off;
+  hdr->n_merges = n_merges;
+  hdr->n_dq_tiles = split ? n_unsplit : n_tiles;
+  hdr->merges_offset = merges_off;
+  hdr->dq_tiles_offset = dq_tiles_off;
+  hdr->dq_slots_offset = dq_slots_off;
+  hdr->ws_rows = ws_rows;
   *bytes = size_t(total);
   return ZL_OK;
 }

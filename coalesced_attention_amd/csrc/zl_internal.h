@@ -22,6 +22,9 @@ constexpr int kFwdWaves = ZL_FWD_WAVES;
 constexpr int kFwdBlockM = kFwdWaves * 32;
 constexpr int kFwdBlockN = ZL_FWD_BLOCK_N;
 static_assert(kFwdBlockM == 256, "the worklist cuts 256-row tiles");
+static_assert(sizeof(zl_worklist_header) == 192 && sizeof(zl_tile) == 32 &&
+                  sizeof(zl_outmap) == 16 && sizeof(zl_merge) == 32,
+              "ABI record sizes");
 // dK/dV backward tile: 4 producer / consumer wave pairs x 32 keys, streaming
 // 32 query rows per step.
 constexpr int kBwdPairs = 4;
@@ -33,6 +36,12 @@ constexpr int kBwdBlockM = 32;
 constexpr int kCostC0PerRow = 64;
 // Largest static slot count accepted by zl_build_worklist.
 constexpr int kMaxSlots = 1 << 20;
+
+// Merge the key-chunk partials of every split item of a worklist (its merge
+// list) from the forward workspace into O / LSE, one launch on `stream`.
+// Defined with the merge kernel; h is the host header, d_wl the device copy.
+int launch_merge_list(const zl_worklist_header* h, const char* d_wl, const float* ws_o,
+                      const float* ws_lse, float* o, float* lse, void* stream);
 
 // Record a printf-style detail for zl_last_error() and return `code`.
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));

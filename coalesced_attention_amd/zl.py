@@ -43,7 +43,7 @@ class Item(ctypes.Structure):
 class Problem(ctypes.Structure):
     _fields_ = [("q_rows", ctypes.c_int64), ("kv_rows", ctypes.c_int64),
                 ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("reserved", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("kv_chunk", ctypes.c_int32)]
 
 
 class Tile(ctypes.Structure):
@@ -63,14 +63,22 @@ class WorklistHeader(ctypes.Structure):
                 ("slots_offset", ctypes.c_uint64), ("total_cost", ctypes.c_int64),
                 ("max_slot_cost", ctypes.c_int64), ("block_n_bwd", ctypes.c_int32),
                 ("n_bwd_tiles", ctypes.c_int32), ("bwd_tiles_offset", ctypes.c_uint64),
-                ("bwd_slots_offset", ctypes.c_uint64), ("bwd_max_slot_cost", ctypes.c_int64)]
+                ("bwd_slots_offset", ctypes.c_uint64), ("bwd_max_slot_cost", ctypes.c_int64),
+                ("kv_chunk", ctypes.c_int32), ("n_vitems", ctypes.c_int32),
+                ("outmap_offset", ctypes.c_uint64), ("n_merges", ctypes.c_int32),
+                ("n_dq_tiles", ctypes.c_int32), ("merges_offset", ctypes.c_uint64),
+                ("dq_tiles_offset", ctypes.c_uint64), ("dq_slots_offset", ctypes.c_uint64),
+                ("ws_rows", ctypes.c_int64), ("pad", ctypes.c_uint8 * 8)]
 
 
 TILE_DTYPE = np.dtype([("q_row0", "<i8"), ("kv_row0", "<i8"), ("q_rows", "<i4"),
                        ("kv_len", "<i4"), ("head", "<i4"), ("item", "<i4")])
+OUTMAP_DTYPE = np.dtype([("o_shift", "<i8"), ("to_workspace", "<i4"), ("reserved", "<i4")])
+MERGE_DTYPE = np.dtype([("q_off", "<i8"), ("ws_row0", "<i8"), ("q_len", "<i4"),
+                        ("head_begin", "<i4"), ("head_cnt", "<i4"), ("n_parts", "<i4")])
 
 assert ctypes.sizeof(Item) == 32 and ctypes.sizeof(Tile) == 32
-assert ctypes.sizeof(WorklistHeader) == 128 and ctypes.sizeof(Problem) == 32
+assert ctypes.sizeof(WorklistHeader) == 192 and ctypes.sizeof(Problem) == 32
 
 
 def _load() -> ctypes.CDLL:
@@ -94,7 +102,7 @@ def _load() -> ctypes.CDLL:
     lib.zl_build_worklist.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Item), i32, i32, vp,
                                       ctypes.POINTER(ctypes.c_size_t)]
     lib.zl_coalesced_attn_fwd.restype = ctypes.c_int
-    lib.zl_coalesced_attn_fwd.argtypes = [vp, vp, vp, vp, vp, fp, fp, vp]
+    lib.zl_coalesced_attn_fwd.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, vp]
     lib.zl_merge_partials.restype = ctypes.c_int
     lib.zl_merge_partials.argtypes = [i32, i64, i32, i32, i32, i32, fp, fp, i64, fp, fp, vp]
     lib.zl_coalesced_attn_bwd.restype = ctypes.c_int
@@ -159,6 +167,34 @@ class Worklist:
         off = h.bwd_slots_offset
         return self.host[off:off + 4 * (h.n_slots + 1)].view(np.int32)
 
+    def dq_tiles(self) -> np.ndarray:
+        h = self.header
+        off = h.dq_tiles_offset
+        return self.host[off:off + h.n_dq_tiles * 32].view(TILE_DTYPE)
+
+    def dq_slots(self) -> np.ndarray:
+        h = self.header
+        if h.n_slots == 0:
+            return np.zeros(0, np.int32)
+        off = h.dq_slots_offset
+        return self.host[off:off + 4 * (h.n_slots + 1)].view(np.int32)
+
+    def outmap(self) -> np.ndarray:
+        h = self.header
+        off = h.outmap_offset
+        return self.host[off:off + h.n_vitems * 16].view(OUTMAP_DTYPE)
+
+    def merges(self) -> np.ndarray:
+        h = self.header
+        off = h.merges_offset
+        return self.host[off:off + h.n_merges * 32].view(MERGE_DTYPE)
+
+    @property
+    def workspace_floats(self) -> int:
+        """fp32 elements of the forward workspace (0 when nothing is split)."""
+        h = self.header
+        return h.ws_rows * h.num_heads * (h.head_dim + 1)
+
     def to(self, device) -> "Worklist":
         import torch
         self.device = torch.from_numpy(self.host).to(device)
@@ -175,12 +211,14 @@ def default_slots(device=None) -> int:
 
 
 def build_worklist(items: Iterable, q_rows: int, kv_rows: int, num_heads: int, head_dim: int,
-                   softmax_scale: float = 0.0, n_slots: int = 0, device=None) -> Worklist:
+                   softmax_scale: float = 0.0, n_slots: int = 0, device=None,
+                   kv_chunk: int = 0) -> Worklist:
     """zl_build_worklist. ``items`` are (q_off, q_len, kv_off, kv_len,
     head_begin, head_cnt) tuples or objects with ``as_tuple()``. With
-    ``device`` the worklist is also copied there."""
+    ``device`` the worklist is also copied there; ``kv_chunk`` > 0 splits
+    items with more keys into key chunks merged inside the forward."""
     arr, n = _items_array(items)
-    prob = Problem(q_rows, kv_rows, num_heads, head_dim, softmax_scale, 0)
+    prob = Problem(q_rows, kv_rows, num_heads, head_dim, softmax_scale, kv_chunk)
     nbytes = ctypes.c_size_t(0)
     _check(lib.zl_build_worklist(ctypes.byref(prob), arr, n, n_slots, None, ctypes.byref(nbytes)),
            "zl_build_worklist(size)")
@@ -211,9 +249,11 @@ def _check_qkv(wl: Worklist, q, k, v):
                              f"{(rows, h.num_heads, h.head_dim)}")
 
 
-def coalesced_attn_fwd(wl: Worklist, q, k, v, o=None, lse=None, stream=None):
+def coalesced_attn_fwd(wl: Worklist, q, k, v, o=None, lse=None, stream=None, workspace=None):
     """zl_coalesced_attn_fwd. Returns (o [q_rows, H, d] fp32, lse [q_rows, H] fp32).
-    Rows no item covers are left as they were in ``o``/``lse``."""
+    Rows no item covers are left as they were in ``o``/``lse``. A worklist
+    that splits items needs a workspace of ``wl.workspace_floats`` fp32
+    (allocated here when not given)."""
     import torch
     _check_qkv(wl, q, k, v)
     h = wl.header
@@ -228,8 +268,16 @@ def coalesced_attn_fwd(wl: Worklist, q, k, v, o=None, lse=None, stream=None):
         raise ValueError("o and lse must be contiguous fp32")
     if tuple(o.shape) != (h.q_rows, h.num_heads, h.head_dim) or tuple(lse.shape) != (h.q_rows, h.num_heads):
         raise ValueError("o / lse shape does not match the worklist")
+    ws_ptr = None
+    if wl.workspace_floats > 0:
+        if workspace is None:
+            workspace = torch.empty(wl.workspace_floats, dtype=torch.float32, device=q.device)
+        if workspace.dtype != torch.float32 or not workspace.is_contiguous() \
+                or workspace.numel() < wl.workspace_floats:
+            raise ValueError(f"workspace must be contiguous fp32 with >= {wl.workspace_floats} elements")
+        ws_ptr = workspace.data_ptr()
     _check(lib.zl_coalesced_attn_fwd(wl.host_ptr(), wl.device.data_ptr(), q.data_ptr(), k.data_ptr(),
-                                     v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                     v.data_ptr(), o.data_ptr(), lse.data_ptr(), ws_ptr,
                                      _stream_handle(stream, q.device)), "zl_coalesced_attn_fwd")
     return o, lse
 

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define ZL_ABI_VERSION 2
+#define ZL_ABI_VERSION 3
 #define ZL_WORKLIST_MAGIC 0x31574c5au /* "ZLW1" little-endian */
 
 enum zl_status {
@@ -69,21 +69,34 @@ typedef struct zl_item {
 } zl_item;
 
 /* Shapes shared by every item of one launch. softmax_scale <= 0 selects
- * 1/sqrt(head_dim). */
+ * 1/sqrt(head_dim).
+ * kv_chunk > 0 splits, inside the forward launch, every item with more than
+ * kv_chunk keys into n = ceil(kv_len / kv_chunk) key chunks of equal length
+ * (rounded up to a multiple of 64; the last one shorter): each chunk is
+ * computed as its own partial (O_p, LSE_p) in a caller workspace and the
+ * partials are then merged exactly as zl_merge_partials does (a theta k
+ * split done inside one rank: pith.science review, "What carries the
+ * argument"). This shortens the longest tiles, so the static schedule
+ * balances better. kv_chunk = 0: no split. */
 typedef struct zl_problem {
   int64_t q_rows;
   int64_t kv_rows;
   int32_t num_heads;
   int32_t head_dim;
   float softmax_scale;
-  int32_t reserved; /* must be 0 */
+  int32_t kv_chunk; /* >= 0 */
 } zl_problem;
 
-/* Worklist buffer = header, then tiles, then slot offsets.
+/* Worklist buffer = header, then sections at the header's offsets (each
+ * 256-byte aligned): forward tiles and slot offsets, backward tiles and slot
+ * offsets, the output map, the merge list, and (when items are split) the
+ * unsplit forward tiles and slot offsets for the dQ pass.
  * A forward tile is block_m query rows of one item on one head, against the
- * item's whole key range. Tiles are ordered by the stable LPT rule: cost =
- * q_rows * kv_len + cost_c0, sorted by cost, largest first, ties kept in
- * (item, head, query block) order; with n_slots > 0 each tile in that order
+ * item's whole key range (or one key chunk of it, see kv_chunk). Tiles are
+ * ordered by the stable LPT rule: cost = q_rows * kv_len + cost_c0, sorted by
+ * cost, largest first, ties kept in cut order: the unsplit items' tiles in
+ * (item, head, query block) order, then the chunks' tiles in (item, chunk,
+ * head, query block) order; with n_slots > 0 each tile in that order
  * goes to the least-loaded slot (lowest index on ties) and the tile array
  * is stored slot by slot, slot s owning tiles [slots[s], slots[s+1]). With
  * n_slots == 0 the tile array is the LPT order and the launch has one
@@ -97,8 +110,31 @@ typedef struct zl_tile {
   int32_t q_rows;  /* 1..block_m */
   int32_t kv_len;  /* >= 0 */
   int32_t head;
-  int32_t item;
+  int32_t item;    /* item, or n_items + k for the k-th key chunk of a split item */
 } zl_tile;
+
+/* Where a forward tile writes: rows q_row0 .. of O / LSE (to_workspace = 0)
+ * or of the workspace partials (to_workspace = 1), shifted by o_shift rows.
+ * One entry per item and per key chunk of a split item (indexed by
+ * zl_tile.item). 16 bytes. */
+typedef struct zl_outmap {
+  int64_t o_shift;
+  int32_t to_workspace;
+  int32_t reserved;
+} zl_outmap;
+
+/* One split item: its n_parts partials sit at workspace rows
+ * ws_row0 + p * q_len (p = 0 .. n_parts-1) and are merged into O / LSE rows
+ * q_off .. q_off + q_len on heads [head_begin, head_begin + head_cnt).
+ * 32 bytes. */
+typedef struct zl_merge {
+  int64_t q_off;
+  int64_t ws_row0;
+  int32_t q_len;
+  int32_t head_begin;
+  int32_t head_cnt;
+  int32_t n_parts;
+} zl_merge;
 
 typedef struct zl_worklist_header {
   uint32_t magic;       /* ZL_WORKLIST_MAGIC */
@@ -129,7 +165,23 @@ typedef struct zl_worklist_header {
   uint64_t bwd_tiles_offset;
   uint64_t bwd_slots_offset;
   int64_t bwd_max_slot_cost;
-} zl_worklist_header; /* 128 bytes */
+  /* In-launch key split (problem.kv_chunk). The forward tiles above then
+   * include the chunks' tiles; the backward's query-major dQ pass uses the
+   * unsplit forward schedule at dq_tiles_offset (n_dq_tiles tiles, int32
+   * slot offsets at dq_slots_offset), which is the forward section itself
+   * when nothing is split. outmap: n_vitems zl_outmap entries; merges:
+   * n_merges zl_merge entries; ws_rows: rows of the forward workspace. */
+  int32_t kv_chunk;
+  int32_t n_vitems;
+  uint64_t outmap_offset;
+  int32_t n_merges;
+  int32_t n_dq_tiles;
+  uint64_t merges_offset;
+  uint64_t dq_tiles_offset;
+  uint64_t dq_slots_offset;
+  int64_t ws_rows;
+  uint8_t pad[8];
+} zl_worklist_header; /* 192 bytes */
 
 int zl_abi_version(void);
 const char* zl_status_string(int status);
@@ -144,7 +196,8 @@ const char* zl_last_error(void);
  * The caller copies the buffer to device memory unchanged; a worklist is
  * immutable and can serve any number of launches (every layer of a step).
  * Errors: ZL_ERR_NULL, ZL_ERR_SHAPE, ZL_ERR_RANGE, ZL_ERR_OVERLAP,
- * ZL_ERR_BUFSIZE, ZL_ERR_ARG (n_items < 0, n_slots < 0 or > 1<<20).
+ * ZL_ERR_BUFSIZE, ZL_ERR_ARG (n_items < 0, n_slots < 0 or > 1<<20,
+ * kv_chunk < 0).
  * The schedule is the stable LPT reading of "stably schedules and fuses
  * whole sequences and distributed-attention shards on shared ranks"
  * (pith.science review of arXiv 2608.01150, "What carries the argument"). */
@@ -159,10 +212,14 @@ int zl_build_worklist(const zl_problem* problem, const zl_item* items, int32_t n
  * h_wl: the worklist in host memory (read for the launch shape); d_wl: the
  * same bytes in device memory. q, k, v: bf16 device buffers; o, lse: fp32
  * device buffers. Only (row, head) pairs that some item covers are written.
- * Asynchronous on `stream`. Errors: ZL_ERR_NULL, ZL_ERR_WORKLIST,
- * ZL_ERR_ALIGN, ZL_ERR_HIP. */
+ * workspace: fp32 device buffer of ws_rows * num_heads * (head_dim + 1)
+ * floats (partial O [ws_rows, H, d], then partial LSE [ws_rows, H]) when the
+ * worklist splits items (header ws_rows > 0), else ignored (may be NULL);
+ * owned by the caller, overwritten. Split items cost one more launch (the
+ * merge) on the same stream. Asynchronous on `stream`. Errors: ZL_ERR_NULL,
+ * ZL_ERR_WORKLIST, ZL_ERR_ALIGN, ZL_ERR_HIP. */
 int zl_coalesced_attn_fwd(const void* h_wl, const void* d_wl, const void* q, const void* k,
-                          const void* v, float* o, float* lse, void* stream);
+                          const void* v, float* o, float* lse, float* workspace, void* stream);
 
 /* Merge of KV-split partials. A k-split shard computes attention of the
  * same queries against disjoint key ranges (pith.science review, "What

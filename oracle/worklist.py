@@ -23,6 +23,16 @@ one item on one head against all of the item's queries, cost = keys *
 q_len + c0, scheduled by the same rule. Its tiles are cut in the order
 (item, key block, head), so equal-cost ties run through the heads first.
 
+Key split inside a launch (a theta k split of one item on one rank, same
+section): with ``kv_chunk`` > 0 an item with queries and more than
+kv_chunk keys is cut into n = ceil(kv_len / kv_chunk) key chunks of
+ceil(kv_len / n) keys rounded up to a multiple of 64 (the last chunk
+shorter; n then recounted). Chunk p of the k-th split item (in item order)
+is numbered n_items + (chunks of earlier split items) + p; its tiles are cut
+after all unsplit items' tiles, in (chunk, head, query block) order, and
+its partial output goes to workspace rows ws_row0 + p * q_len, ws_row0
+being the rows of earlier split items.
+
 Python's ``sorted`` is stable and the slot search is a plain scan, so the
 result can be checked against the C++ builder bit for bit.
 """
@@ -42,24 +52,68 @@ class Tile(NamedTuple):
     cost: int
 
 
-def cut_tiles(items: Iterable, block_m: int, c0: int) -> List[Tile]:
+def _tuple(it):
+    return it.as_tuple() if hasattr(it, "as_tuple") else tuple(int(x) for x in it)
+
+
+def split_parts(q_len: int, kv_len: int, head_cnt: int, kv_chunk: int) -> Tuple[int, int]:
+    """(number of key chunks, keys per chunk) of one item; (1, 0) when the
+    item is not split."""
+    if kv_chunk <= 0 or q_len <= 0 or head_cnt <= 0 or kv_len <= kv_chunk:
+        return 1, 0
+    n = -(-kv_len // kv_chunk)
+    chunk = -(-(-(-kv_len // n)) // 64) * 64
+    return -(-kv_len // chunk), chunk
+
+
+def split_plan(items: Iterable, kv_chunk: int):
+    """Output map [(o_shift, to_workspace)] per item and chunk, merge list
+    [(q_off, ws_row0, q_len, head_begin, head_cnt, n_parts)] and workspace
+    rows of the key split."""
+    items = [_tuple(it) for it in items]
+    outmap = [(0, 0)] * len(items)
+    merges, ws = [], 0
+    for q_off, q_len, kv_off, kv_len, h0, hc in items:
+        n, _ = split_parts(q_len, kv_len, hc, kv_chunk)
+        if n == 1:
+            continue
+        merges.append((q_off, ws, q_len, h0, hc, n))
+        outmap += [(ws + p * q_len - q_off, 1) for p in range(n)]
+        ws += n * q_len
+    return outmap, merges, ws
+
+
+def cut_tiles(items: Iterable, block_m: int, c0: int, kv_chunk: int = 0) -> List[Tile]:
+    items = [_tuple(it) for it in items]
     tiles = []
-    for idx, it in enumerate(items):
-        q_off, q_len, kv_off, kv_len, h0, hc = (it.as_tuple() if hasattr(it, "as_tuple")
-                                                else tuple(int(x) for x in it))
+
+    def cut(idx, vitem, k0, keys):
+        q_off, q_len, kv_off, kv_len, h0, hc = items[idx]
         for h in range(h0, h0 + hc):
             for r0 in range(0, q_len, block_m):
                 rows = min(block_m, q_len - r0)
-                tiles.append(Tile(q_off + r0, kv_off, rows, kv_len, h, idx,
-                                  rows * kv_len + c0))
+                tiles.append(Tile(q_off + r0, kv_off + k0, rows, keys, h, vitem,
+                                  rows * keys + c0))
+
+    plan = [split_parts(it[1], it[3], it[5], kv_chunk) for it in items]
+    for idx, it in enumerate(items):
+        if plan[idx][0] == 1:
+            cut(idx, idx, 0, it[3])
+    vitem = len(items)
+    for idx, it in enumerate(items):
+        n, chunk = plan[idx]
+        if n == 1:
+            continue
+        for p in range(n):
+            cut(idx, vitem, p * chunk, min(chunk, it[3] - p * chunk))
+            vitem += 1
     return tiles
 
 
 def cut_bwd_tiles(items: Iterable, block_n: int, c0: int) -> List[Tile]:
     tiles = []
     for idx, it in enumerate(items):
-        q_off, q_len, kv_off, kv_len, h0, hc = (it.as_tuple() if hasattr(it, "as_tuple")
-                                                else tuple(int(x) for x in it))
+        q_off, q_len, kv_off, kv_len, h0, hc = _tuple(it)
         if q_len == 0:
             continue
         for k0 in range(0, kv_len, block_n):
@@ -88,11 +142,11 @@ def lpt(tiles: List[Tile], n_slots: int) -> Tuple[List[Tile], List[int], List[in
     return flat, begin, loads
 
 
-def lpt_schedule(items: Iterable, block_m: int, n_slots: int, c0: int
+def lpt_schedule(items: Iterable, block_m: int, n_slots: int, c0: int, kv_chunk: int = 0
                  ) -> Tuple[List[Tile], List[int], List[int]]:
     """Forward schedule: (tiles in schedule order, slot_begin offsets
     [n_slots+1], slot loads). For n_slots == 0: (tiles in LPT order, [], [])."""
-    return lpt(cut_tiles(items, block_m, c0), n_slots)
+    return lpt(cut_tiles(items, block_m, c0, kv_chunk), n_slots)
 
 
 def lpt_schedule_bwd(items: Iterable, block_n: int, n_slots: int, c0: int

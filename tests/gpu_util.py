@@ -73,13 +73,13 @@ def to_device(inp: W.Inputs, device="cuda"):
     return (inp.q.to(device), inp.k.to(device), inp.v.to(device))
 
 
-def run_fwd(items, q, k, v, num_heads, head_dim, n_slots=256, poison=True):
+def run_fwd(items, q, k, v, num_heads, head_dim, n_slots=256, poison=True, kv_chunk=0):
     """Build a worklist and run the forward; O and LSE start as NaN so that
     unwritten entries stay visible."""
     import torch
     from coalesced_attention_amd import zl
     wl = zl.build_worklist(items, q.shape[0], k.shape[0], num_heads, head_dim, n_slots=n_slots,
-                           device=q.device)
+                           device=q.device, kv_chunk=kv_chunk)
     o = torch.full((q.shape[0], num_heads, head_dim), float("nan"), device=q.device)
     lse = torch.full((q.shape[0], num_heads), float("nan"), device=q.device)
     zl.coalesced_attn_fwd(wl, q, k, v, o, lse)

@@ -11,7 +11,7 @@ import pytest
 
 from coalesced_attention_amd import workloads as W
 from coalesced_attention_amd import zl
-from oracle.worklist import lpt_schedule, lpt_schedule_bwd
+from oracle.worklist import lpt_schedule, lpt_schedule_bwd, split_plan
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "zl.h")
@@ -67,6 +67,45 @@ def test_worklist_matches_reference_schedule(cfg, n_slots):
     assert np.array_equal(bgot, bwant)
     if n_slots:
         assert list(built.bwd_slots()) == bbegin and h.bwd_max_slot_cost == max(bloads)
+    # no key split: the dQ pass reuses the forward section, every item maps to O
+    assert (h.dq_tiles_offset, h.dq_slots_offset, h.n_dq_tiles) == (h.tiles_offset, h.slots_offset, h.n_tiles)
+    assert h.n_merges == 0 and h.ws_rows == 0 and h.n_vitems == len(wl.items)
+    assert not built.outmap()["to_workspace"].any() and not built.outmap()["o_shift"].any()
+
+
+def _tile_array(tiles):
+    return np.array([(t.q_row0, t.kv_row0, t.q_rows, t.kv_len, t.head, t.item) for t in tiles],
+                    dtype=zl.TILE_DTYPE)
+
+
+@pytest.mark.parametrize("cfg,kv_chunk,n_slots", [(0, 64, 0), (0, 64, 3), (0, 100, 7), (2, 8192, 256),
+                                                  (3, 27456, 256), (3, 40000, 97), (3, 1 << 20, 256)])
+def test_key_split_worklist_matches_reference(cfg, kv_chunk, n_slots):
+    wl = W.config(cfg)
+    built = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim,
+                              n_slots=n_slots, kv_chunk=kv_chunk)
+    h = built.header
+    assert h.kv_chunk == kv_chunk
+    ref, begin, loads = lpt_schedule(wl.items, h.block_m, n_slots, h.cost_c0, kv_chunk)
+    assert h.n_tiles == len(ref) and np.array_equal(built.tiles(), _tile_array(ref))
+    if n_slots:
+        assert list(built.slots()) == begin and h.max_slot_cost == max(loads)
+    outmap, merges, ws = split_plan(wl.items, kv_chunk)
+    om = built.outmap()
+    assert h.n_vitems == len(outmap)
+    assert [(int(a), int(b)) for a, b in zip(om["o_shift"], om["to_workspace"])] == outmap
+    got_m = built.merges()
+    assert h.n_merges == len(merges)
+    assert [tuple(int(x) for x in m) for m in got_m.tolist()] == merges
+    assert h.ws_rows == ws
+    assert built.workspace_floats == ws * wl.num_heads * (wl.head_dim + 1)
+    # the dQ pass runs the unsplit forward schedule
+    uref, ubegin, _ = lpt_schedule(wl.items, h.block_m, n_slots, h.cost_c0)
+    assert h.n_dq_tiles == len(uref) and np.array_equal(built.dq_tiles(), _tile_array(uref))
+    if n_slots:
+        assert list(built.dq_slots()) == ubegin
+    if merges:
+        assert h.dq_tiles_offset not in (h.tiles_offset,)
 
 
 def test_worklist_is_deterministic():
@@ -76,10 +115,10 @@ def test_worklist_is_deterministic():
     assert np.array_equal(a.host, b.host)
 
 
-def _rc_build(items, q_rows=1000, kv_rows=1000, H=4, d=128, n_slots=0, scale=0.0, reserved=0,
+def _rc_build(items, q_rows=1000, kv_rows=1000, H=4, d=128, n_slots=0, scale=0.0, kv_chunk=0,
               buf=True, nbytes=None):
     arr, n = zl._items_array(items)
-    prob = zl.Problem(q_rows, kv_rows, H, d, scale, reserved)
+    prob = zl.Problem(q_rows, kv_rows, H, d, scale, kv_chunk)
     size = ctypes.c_size_t(0)
     rc = zl.lib.zl_build_worklist(ctypes.byref(prob), arr, n, n_slots, None, ctypes.byref(size))
     if rc or not buf:
@@ -102,7 +141,8 @@ def test_build_errors():
     assert _rc_build([(0, 10, 0, 10, 0, 2), (5, 10, 0, 10, 2, 2)]) == 0    # disjoint heads
     assert _rc_build([(0, 10, 0, 10, 0, 4), (10, 10, 0, 10, 0, 4)]) == 0   # adjacent rows
     assert _rc_build(ok, n_slots=-1) == -9
-    assert _rc_build(ok, reserved=1) == -9
+    assert _rc_build(ok, kv_chunk=-1) == -9
+    assert _rc_build(ok, kv_chunk=1) == 0
     assert _rc_build(ok, nbytes=64) == -5
     assert _rc_build(ok, scale=float("inf")) == -9
     prob = zl.Problem(10, 10, 1, 64, 0.0, 0)
@@ -124,18 +164,25 @@ def test_fwd_and_merge_reject_bad_arguments_before_any_hip_call():
     built = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim)
     p = 1 << 20  # aligned fake device address; never dereferenced on these paths
     f = zl.lib.zl_coalesced_attn_fwd
-    assert f(None, p, p, p, p, p, p, None) == -1
-    assert f(built.host_ptr(), None, p, p, p, p, p, None) == -1
-    assert f(built.host_ptr(), p, p + 8, p, p, p, p, None) == -6
+    assert f(None, p, p, p, p, p, p, None, None) == -1
+    assert f(built.host_ptr(), None, p, p, p, p, p, None, None) == -1
+    assert f(built.host_ptr(), p, p + 8, p, p, p, p, None, None) == -6
     bad = built.host.copy()
     bad[:4] = 0
-    assert f(bad.ctypes.data, p, p, p, p, p, p, None) == -7
+    assert f(bad.ctypes.data, p, p, p, p, p, p, None, None) == -7
     bad = built.host.copy()
     bad.view(np.uint32)[1] = 99  # abi version
-    assert f(bad.ctypes.data, p, p, p, p, p, p, None) == -7
+    assert f(bad.ctypes.data, p, p, p, p, p, p, None, None) == -7
     bad = built.host.copy()
     zl.WorklistHeader.from_buffer(bad).total_bytes = 64
-    assert f(bad.ctypes.data, p, p, p, p, p, p, None) == -7
+    assert f(bad.ctypes.data, p, p, p, p, p, p, None, None) == -7
+    bad = built.host.copy()
+    zl.WorklistHeader.from_buffer(bad).n_merges = 1  # merges without a workspace size
+    assert f(bad.ctypes.data, p, p, p, p, p, p, None, None) == -7
+    split = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim, kv_chunk=64)
+    assert split.header.ws_rows > 0
+    assert f(split.host_ptr(), p, p, p, p, p, p, None, None) == -1       # workspace required
+    assert f(split.host_ptr(), p, p, p, p, p, p, p + 4, None) == -6      # and aligned
     m = zl.lib.zl_merge_partials
     assert m(2, 10, 4, 0, 4, 128, None, p, 10, p, p, None) == -1
     assert m(2, 10, 4, 0, 4, 96, p, p, 10, p, p, None) == -2

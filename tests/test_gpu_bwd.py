@@ -30,9 +30,10 @@ def _gpu():
     from coalesced_attention_amd import zl  # noqa: F401
 
 
-def _run(items, q, k, v, dout, H, d, n_slots=256):
+def _run(items, q, k, v, dout, H, d, n_slots=256, kv_chunk=0):
     from coalesced_attention_amd import zl
-    wl = zl.build_worklist(items, q.shape[0], k.shape[0], H, d, n_slots=n_slots, device=q.device)
+    wl = zl.build_worklist(items, q.shape[0], k.shape[0], H, d, n_slots=n_slots, device=q.device,
+                           kv_chunk=kv_chunk)
     o, lse = zl.coalesced_attn_fwd(wl, q, k, v)
     dq, dk, dv = zl.coalesced_attn_bwd(wl, q, k, v, o, lse, dout)
     torch.cuda.synchronize()
@@ -68,11 +69,14 @@ def _oracle_all(items, Q, K, V, dO, scale):
     return orc.coalesced_backward(Q, K, V, dO, items, scale)
 
 
-def test_backward_tiny_workload_shared_kv():
+@pytest.mark.parametrize("kv_chunk", [0, 64])
+def test_backward_tiny_workload_shared_kv(kv_chunk):
+    """kv_chunk 64: the forward splits and merges key chunks; the backward
+    runs the unsplit schedule on the merged O and LSE."""
     wl = W.config(0)
     inp = W.make_inputs(wl)
     q, k, v, g = (x.cuda() for x in (inp.q, inp.k, inp.v, inp.dout))
-    dq, dk, dv = _run(wl.items, q, k, v, g, wl.num_heads, wl.head_dim)
+    dq, dk, dv = _run(wl.items, q, k, v, g, wl.num_heads, wl.head_dim, kv_chunk=kv_chunk)
     Qh, Kh, Vh, Gh = (x.double().numpy() for x in (inp.q, inp.k, inp.v, inp.dout))
     rq, rk, rv = _oracle_all(wl.items, Qh, Kh, Vh, Gh, wl.softmax_scale)
     gate = Gate("config 0 backward")

@@ -43,16 +43,21 @@ def _host(x):
 # ----------------------------------------------------------------- configs
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("c", [0, 1, 2, 3])
-def test_forward_parity(c):
+@pytest.mark.parametrize("c,kv_chunk", [(0, 0), (1, 0), (2, 0), (3, 0), (0, 64), (3, 27456)])
+def test_forward_parity(c, kv_chunk):
+    """Every config against the oracle; with kv_chunk > 0 the long items are
+    split into key chunks inside the launch and merged (config 3's 109,800
+    keys into 4 chunks of 27,456; config 0's items into 64-key chunks)."""
     wl, inp, (q, k, v) = _workload(c)
-    log(f"config {c}: forward on GPU, {len(wl.items)} items")
-    built, o, lse = run_fwd(wl.items, q, k, v, wl.num_heads, wl.head_dim)
+    log(f"config {c}: forward on GPU, {len(wl.items)} items, kv_chunk {kv_chunk}")
+    built, o, lse = run_fwd(wl.items, q, k, v, wl.num_heads, wl.head_dim, kv_chunk=kv_chunk)
+    if kv_chunk:
+        assert built.header.n_merges > 0
     O, LSE = o.cpu().numpy(), lse.cpu().numpy()
     log(f"config {c}: {built.n_tiles} tiles done; oracle check")
     st = oracle_compare(Stats(), wl.items, _host(inp.q), _host(inp.k), _host(inp.v), O, LSE,
                         wl.softmax_scale, seed=c)
-    st.assert_gates(f"config {c} forward")
+    st.assert_gates(f"config {c} forward (kv_chunk {kv_chunk})")
     # every covered (row, head) written, nothing else
     cov = np.zeros((wl.q_rows, wl.num_heads), bool)
     for it in wl.items:
@@ -136,6 +141,24 @@ def test_bitwise_determinism_and_schedule_independence():
     for o2, l2 in outs[1:]:
         assert np.array_equal(o2, outs[0][0], equal_nan=True)
         assert np.array_equal(l2, outs[0][1], equal_nan=True)
+
+
+def test_key_split_bitwise_over_slot_counts_and_close_to_unsplit():
+    """A split forward is bitwise the same for any slot count (every chunk is
+    computed by one tile and merged in chunk order), and within rounding of
+    the unsplit forward."""
+    wl, inp, (q, k, v) = _workload(0)
+    outs = []
+    for n_slots in (256, 0, 7, 1):
+        _, o, lse = run_fwd(wl.items, q, k, v, wl.num_heads, wl.head_dim, n_slots=n_slots, kv_chunk=64)
+        outs.append((o.cpu().numpy(), lse.cpu().numpy()))
+    for o2, l2 in outs[1:]:
+        assert np.array_equal(o2, outs[0][0], equal_nan=True)
+        assert np.array_equal(l2, outs[0][1], equal_nan=True)
+    _, o, lse = run_fwd(wl.items, q, k, v, wl.num_heads, wl.head_dim)
+    O, LSE = o.cpu().numpy(), lse.cpu().numpy()
+    assert np.nanmax(np.abs(outs[0][0] - O)) < 5e-3
+    assert np.nanmax(np.abs(outs[0][1] - LSE)) < 1e-5
 
 
 def test_independence_across_packed_sequences():

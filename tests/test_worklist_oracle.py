@@ -94,3 +94,57 @@ def test_backward_tiles_cover_every_key_head_pair_once():
             for r in range(it[3]) for h in range(it[4], it[4] + it[5])}
     assert set(cov) == want and set(cov.values()) == {1}
     assert loads == [sum(t.cost for t in tiles[begin[s]:begin[s + 1]]) for s in range(5)]
+
+
+@pytest.mark.parametrize("cfg,kv_chunk", [(0, 64), (0, 100), (3, 27456)])
+def test_key_split_covers_every_key_once(cfg, kv_chunk):
+    """With a key split every (query row, head, key) triple of every item is
+    still covered by exactly one forward tile, and each item's chunk tiles
+    write to its own workspace rows."""
+    from oracle.worklist import cut_tiles, split_parts, split_plan
+    from coalesced_attention_amd import workloads as W
+    wl = W.config(cfg)
+    items = [it.as_tuple() for it in wl.items]
+    tiles = cut_tiles(items, 256, 0, kv_chunk)
+    outmap, merges, ws = split_plan(items, kv_chunk)
+    n = len(items)
+    # chunk item index -> original item
+    vit = {}
+    v = n
+    for idx, it in enumerate(items):
+        p, _ = split_parts(it[1], it[3], it[5], kv_chunk)
+        if p > 1:
+            for _ in range(p):
+                vit[v] = idx
+                v += 1
+    assert v == len(outmap)
+    if cfg == 3:
+        # count (row-block, head, key) coverage per item by key ranges only
+        for idx, it in enumerate(items):
+            q_off, q_len, kv_off, kv_len, h0, hc = it
+            mine = [t for t in tiles if (t.item == idx or vit.get(t.item) == idx)]
+            for h in range(h0, h0 + hc):
+                for r0 in range(0, q_len, 256):
+                    ranges = sorted((t.kv_row0, t.kv_row0 + t.kv_len) for t in mine
+                                    if t.head == h and t.q_row0 == q_off + r0)
+                    pos = kv_off
+                    for a, b in ranges:
+                        assert a == pos and b > a
+                        pos = b
+                    assert pos == kv_off + kv_len
+    else:
+        cover = {}
+        for t in tiles:
+            idx = t.item if t.item < n else vit[t.item]
+            for r in range(t.q_row0, t.q_row0 + t.q_rows):
+                for kk in range(t.kv_row0, t.kv_row0 + t.kv_len):
+                    key = (idx, r, t.head, kk)
+                    cover[key] = cover.get(key, 0) + 1
+        assert set(cover.values()) == {1}
+        want = sum(it[1] * it[3] * it[5] for it in items)
+        assert len(cover) == want
+    # workspace rows of different split items and chunks do not overlap
+    spans = sorted((m[1] + p * m[2], m[1] + (p + 1) * m[2]) for m in merges for p in range(m[5]))
+    for (a, b), (c, d) in zip(spans, spans[1:]):
+        assert b <= c
+    assert (spans[-1][1] if spans else 0) == ws
