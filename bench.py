@@ -46,6 +46,9 @@ def _args():
     ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time")
+    ap.add_argument("--price-table", action="store_true",
+                    help="instead of the bench line: per-(bucket, theta) prices of the workload's items "
+                         "alone and per bucket, against the coalesced launch (additivity check)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (scale reference for FETCH/WRITE_SIZE)")
     return ap.parse_args()
@@ -180,6 +183,51 @@ def _bench_backward(zl, W, dev, stream, n_slots):
             "flops_5gemm": 2.5 * F, "bwd_tiles": built.header.n_bwd_tiles}
 
 
+def _price_table(zl, wl, q, k, v, dev, n_slots):
+    """Per-(bucket, theta) prices on this GPU. A bucket is one item shape
+    (q_len, kv_len, head_cnt); the theta split of a shard shows in that shape.
+    For each bucket: one item alone, and all of the bucket's items in one
+    launch; then the whole mix coalesced. The pages' planner prices a batch
+    as the sum of per-item prices; coalesced / sum says how additive this
+    kernel is."""
+    import torch
+    from collections import OrderedDict
+    stream = torch.cuda.current_stream(dev)
+    o = torch.empty((wl.q_rows, wl.num_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((wl.q_rows, wl.num_heads), dtype=torch.float32, device=dev)
+
+    def timed(items):
+        built = zl.build_worklist(items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim,
+                                  n_slots=n_slots, device=dev)
+        run = lambda: zl.coalesced_attn_fwd(built, q, k, v, o, lse, stream=stream)
+        for _ in range(2):
+            run()
+        torch.cuda.synchronize()
+        ms = _events_ms(run, 3, stream)
+        reps = max(3, min(200, int(60.0 / max(ms, 1e-3))))  # ~60 ms of launches
+        return _events_ms(run, reps, stream)
+
+    buckets = OrderedDict()
+    for it in wl.items:
+        buckets.setdefault((it.q_len, it.kv_len, it.head_cnt), []).append(it)
+    rows = []
+    for (ql, kl, hc), its in buckets.items():
+        single = timed(its[:1])
+        whole = timed(its)
+        rows.append({"q_len": ql, "kv_len": kl, "head_cnt": hc, "count": len(its),
+                     "single_ms": round(single, 4), "bucket_ms": round(whole, 4),
+                     "flops": 4 * ql * kl * hc * wl.head_dim * len(its)})
+    coalesced = timed(wl.items)
+    sum_single = sum(r["single_ms"] * r["count"] for r in rows)
+    sum_bucket = sum(r["bucket_ms"] for r in rows)
+    return {"metric": "coalesced launch time / sum of isolated prices", "workload": wl.name,
+            "n_slots": n_slots, "buckets": rows, "coalesced_ms": round(coalesced, 4),
+            "sum_single_prices_ms": round(sum_single, 4), "sum_bucket_launches_ms": round(sum_bucket, 4),
+            "coalesced_over_single_prices": round(coalesced / sum_single, 4),
+            "coalesced_over_bucket_launches": round(coalesced / sum_bucket, 4),
+            "data": "synthetic"}
+
+
 def main():
     a = _args()
     if a.gpus != 1:
@@ -207,6 +255,9 @@ def main():
     inp = W.make_inputs(wl)
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     n_slots = zl.default_slots(0) if a.n_slots < 0 else a.n_slots
+    if a.price_table:
+        print(json.dumps(_price_table(zl, wl, q, k, v, dev, n_slots)), flush=True)
+        return
 
     t0 = time.perf_counter()
     built = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim,

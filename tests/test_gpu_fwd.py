@@ -177,6 +177,24 @@ def test_independence_across_packed_sequences():
     assert not np.allclose(O1[~mask], O2[~mask])
 
 
+def test_isolated_launches_match_the_coalesced_launch_bitwise():
+    """The price table times items alone and per bucket: each (row, head) is
+    computed by the same tile in the same key order either way, so those
+    launches give the coalesced launch's bits."""
+    wl = W.config(2)
+    items = wl.items[:1] + wl.items[1:3] + wl.items[25:27]
+    inp = W.make_inputs(wl)
+    q, k, v = to_device(inp)
+    _, o, lse = run_fwd(items, q, k, v, wl.num_heads, wl.head_dim)
+    O, LSE = o.cpu().numpy(), lse.cpu().numpy()
+    for part in ([items[0]], items[1:3], items[3:]):
+        _, o1, l1 = run_fwd(part, q, k, v, wl.num_heads, wl.head_dim)
+        O1, L1 = o1.cpu().numpy(), l1.cpu().numpy()
+        for it in part:
+            rs = slice(it.q_off, it.q_off + it.q_len)
+            assert np.array_equal(O1[rs], O[rs]) and np.array_equal(L1[rs], LSE[rs])
+
+
 def test_closed_forms_on_gpu():
     H, d = 3, 128
     kv = 1000
