@@ -226,7 +226,47 @@ def _config4() -> Workload:
         w.num_heads, w.head_dim, w.q_rows, w.kv_rows, w.items, [], [], False, True)
 
 
-_BUILDERS = [_config0, _config1, _config2, _config3, _config4]
+def _config5() -> Workload:
+    # One rank's share of the four-720p-videos + 200-images batch on 16 ranks:
+    # a 10-s 720p video is 41 x 45 x 80 latents (the 61-frame 15-s latent at
+    # 10 s), placed theta = (4, 1, 1), with 13 of the 200 images.
+    H, d = 24, 128
+    L = 41 * 45 * 80
+    items = [theta_item(L, H, (4, 1, 1), (0, 0, 0), 0, 0)]
+    q, kv = items[0].q_len, L
+    for _ in range(13):
+        items.append(_whole(q, kv, 1024, H))
+        q += 1024
+        kv += 1024
+    return Workload(
+        5, "four-720p-videos-rank-share",
+        "one theta=(4,1,1) shard of a 10-s 720p video (41x45x80 latents, 147600 "
+        "tokens): 36900 queries against all 147600 keys, co-located with 13 "
+        "whole 1024-token images (a 16-rank share of four such videos and 200 "
+        "images); 24 heads, d=128",
+        H, d, q, kv, items, [], [], False, False)
+
+
+def _config6() -> Workload:
+    # A 10-s 1080p video: 1920 x 1080 at the same 8x latent and patch 2 gives
+    # 120 x 68 per frame, 41 frames; placed theta = (8, 2, 1).
+    H, d = 24, 128
+    L = 41 * 68 * 120
+    items = [theta_item(L, H, (8, 2, 1), (0, 0, 0), 0, 0)]
+    q, kv = items[0].q_len, L
+    for _ in range(8):
+        items.append(_whole(q, kv, 1024, H))
+        q += 1024
+        kv += 1024
+    return Workload(
+        6, "1080p-shard",
+        "theta=(8,2,1) shard of a 10-s 1080p video (41x68x120 latents, 334560 "
+        "tokens): 41820 queries on 12 of 24 heads against all 334560 keys, "
+        "co-located with 8 whole 1024-token images; d=128",
+        H, d, q, kv, items, [], [], False, False)
+
+
+_BUILDERS = [_config0, _config1, _config2, _config3, _config4, _config5, _config6]
 NUM_CONFIGS = len(_BUILDERS)
 
 

@@ -88,15 +88,15 @@ def run_fwd(items, q, k, v, num_heads, head_dim, n_slots=256, poison=True, kv_ch
 
 
 def oracle_compare(stats: Stats, items, Qh, Kh, Vh, O, LSE, scale, full_limit=1024, seed=0,
-                   heads=None):
+                   heads=None, block=128):
     """Compare GPU O/LSE (numpy) with the oracle on every row of short items
-    and on the sampled rows (first, last, two random per 128-row block) of
-    long ones. Qh/Kh/Vh are the bf16 inputs as float32 numpy arrays."""
+    and on the sampled rows (first, last, two random per ``block``-row block)
+    of long ones. Qh/Kh/Vh are the bf16 inputs as float32 numpy arrays."""
     from oracle.attention import coalesced_forward_rows
     for idx, it in enumerate(items):
         if it.q_len == 0 or it.head_cnt == 0:
             continue
-        rows = W.sample_rows(it, seed=seed, full_limit=full_limit)
+        rows = W.sample_rows(it, seed=seed, block=block, full_limit=full_limit)
         hs = range(it.head_begin, it.head_begin + it.head_cnt) if heads is None else heads(it)
         for h in hs:
             for r0 in range(0, len(rows), 1024):

@@ -39,6 +39,9 @@ EXPECTED = {  # (q_rows, kv_rows, n_items, tiles at 128 rows, forward flops)
     2: (40958, 65528, 57, 7680, 3.632e12),
     3: (71284, 235984, 18, 8232, 3.724e13),
     4: (40958, 65528, 57, 7680, 3.632e12),
+    # 36900 x 147600 x 24 heads + 13 x 1024^2 x 24, and 41820 x 334560 x 12 + 8 x 1024^2 x 24
+    5: (50212, 160912, 14, 289 * 24 + 13 * 8 * 24, 4 * 128 * (36900 * 147600 * 24 + 13 * 1024 ** 2 * 24)),
+    6: (50012, 342752, 9, 327 * 12 + 8 * 8 * 24, 4 * 128 * (41820 * 334560 * 12 + 8 * 1024 ** 2 * 24)),
 }
 
 
