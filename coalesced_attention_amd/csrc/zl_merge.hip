@@ -9,9 +9,10 @@
 //
 // The kernel is a pure stream over HBM: each thread owns 4 consecutive
 // head_dim elements of one (row, head) and reads them from every part with
-// 128-bit loads; consecutive threads cover consecutive addresses. The part
-// weights are recomputed per thread from the n_parts LSE values, which hit
-// in cache after the first thread of the (row, head).
+// 128-bit non-temporal loads (the partials are read once), writing the result
+// with a non-temporal store; consecutive threads cover consecutive addresses.
+// The part weights are recomputed per thread from the n_parts LSE values,
+// which hit in cache after the first thread of the (row, head).
 
 #include <hip/hip_runtime.h>
 
@@ -47,14 +48,14 @@ __device__ __forceinline__ void merge_one(int n_parts, const float* __restrict__
     for (int p = 0; p < n_parts; ++p) {
       const float w = __expf(lse_parts[p * lse_part] - m);
       wsum += w;
-      const f32x4 x = *reinterpret_cast<const f32x4*>(o_parts + p * o_part);
+      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o_parts + p * o_part));
       acc += w * x;
     }
     const float inv = 1.f / wsum;
     acc *= inv;
     lse = m + __logf(wsum);
   }
-  *reinterpret_cast<f32x4*>(o_out) = acc;
+  __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(o_out));
   if (write_lse) *lse_out = lse;
 }
 
@@ -64,19 +65,19 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
     const float* __restrict__ o_parts, const float* __restrict__ lse_parts,
     int64_t part_row_stride, float* __restrict__ o_out, float* __restrict__ lse_out) {
   constexpr int kVec = D / 4;
-  const int64_t gid = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t total = rows * head_cnt * kVec;
-  if (gid >= total) return;
-  const int vec = int(gid % kVec);
-  const int64_t rh = gid / kVec;
-  const int head = head_begin + int(rh % head_cnt);
-  const int64_t row = rh / head_cnt;
-
-  const int64_t lse_idx = row * H + head;
-  const int64_t o_idx = lse_idx * D + vec * 4;
-  const int64_t lse_part = part_row_stride * H;
-  merge_one<D>(n_parts, o_parts + o_idx, lse_parts + lse_idx, lse_part * D, lse_part,
-               o_out + o_idx, lse_out + lse_idx, vec == 0);
+  for (int64_t gid = int64_t(blockIdx.x) * kThreads + threadIdx.x; gid < total;
+       gid += int64_t(gridDim.x) * kThreads) {
+    const int vec = int(gid % kVec);
+    const int64_t rh = gid / kVec;
+    const int head = head_begin + int(rh % head_cnt);
+    const int64_t row = rh / head_cnt;
+    const int64_t lse_idx = row * H + head;
+    const int64_t o_idx = lse_idx * D + vec * 4;
+    const int64_t lse_part = part_row_stride * H;
+    merge_one<D>(n_parts, o_parts + o_idx, lse_parts + lse_idx, lse_part * D, lse_part,
+                 o_out + o_idx, lse_out + lse_idx, vec == 0);
+  }
 }
 
 // The merge list of a worklist: blockIdx.y (striding by gridDim.y) picks a
@@ -142,7 +143,8 @@ extern "C" int zl_merge_partials(int32_t n_parts, int64_t rows, int32_t num_head
     return zl::fail(ZL_ERR_ARG, "merge output overlaps an input or itself");
 
   const int64_t total = rows * head_cnt * (head_dim / 4);
-  const int64_t blocks = (total + kThreads - 1) / kThreads;
+  // a grid-stride loop over at most 16 workgroups per CU
+  const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, 256 * 16);
   if (blocks > INT32_MAX) return zl::fail(ZL_ERR_ARG, "merge too large for one launch");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (head_dim == 128)
