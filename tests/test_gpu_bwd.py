@@ -183,3 +183,26 @@ def test_backward_deterministic_over_slot_counts():
             ref = got
         for a, b in zip(ref, got):
             assert torch.equal(a, b), n_slots
+
+
+@pytest.mark.timeout(600)
+def test_backward_long_key_range_offsets_past_2gb():
+    """Backward of one 200-query item against 2^20 keys on 4 heads (key
+    offsets in bytes pass 2^31), checked on two heads against the oracle."""
+    H, d = 4, 128
+    n_keys = 1 << 20
+    items = [W.Item(0, 200, 0, n_keys, 0, H)]
+    g = torch.Generator(device="cuda").manual_seed(6)
+    q = torch.randn((200, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((n_keys, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((n_keys, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    do = torch.randn((200, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    dq, dk, dv = _run(items, q, k, v, do, H, d)
+    Qh, Kh, Vh, Gh = (x.float().cpu().numpy() for x in (q, k, v, do))
+    gate = Gate("2^20-key backward")
+    for h in (0, 3):
+        rq, rk, rv, _, _ = orc.attention_backward_item(Qh[:, h], Kh[:, h], Vh[:, h], Gh[:, h], 1 / math.sqrt(d))
+        gate.add("dQ", dq[:, h], rq)
+        gate.add("dK", dk[:, h], rk)
+        gate.add("dV", dv[:, h], rv)
+    gate.check()

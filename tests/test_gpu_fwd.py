@@ -282,3 +282,24 @@ def test_key_permutation_within_an_item():
     sl = slice(a.q_off, a.q_off + a.q_len)
     assert (o1[sl] - o2[sl]).abs().max().item() < 2e-3
     assert (l1[sl] - l2[sl]).abs().max().item() < 1e-4
+
+
+@pytest.mark.timeout(600)
+def test_maximum_key_range_and_offsets_past_2gb():
+    """One item with 2^20 keys on 8 heads (K and V are 2 GiB each, so key
+    offsets in bytes pass 2^31) next to a short item placed after it; the
+    forward must match the oracle on sampled rows of both."""
+    H, d = 8, 128
+    n_keys = 1 << 20
+    items = [W.Item(0, 300, 0, n_keys, 0, H), W.Item(300, 40, n_keys, 70, 0, H)]
+    g = torch.Generator(device="cuda").manual_seed(5)
+    q = torch.randn((340, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((n_keys + 70, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((n_keys + 70, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    log("2^20-key item: forward on GPU")
+    _, o, lse = run_fwd(items, q, k, v, H, d)
+    O, LSE = o.cpu().numpy(), lse.cpu().numpy()
+    Qh, Kh, Vh = (x.float().cpu().numpy() for x in (q, k, v))
+    st = oracle_compare(Stats(), items, Qh, Kh, Vh, O, LSE, 1 / math.sqrt(d), full_limit=64,
+                        seed=9)
+    st.assert_gates("2^20-key item forward")
