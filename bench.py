@@ -36,8 +36,8 @@ METRIC = "mixed-batch coalesced attention fwd TFLOP/s and % of bf16 MFMA peak"
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="workload index (2 = mixed rank share)")
     ap.add_argument("--n-slots", type=int, default=-1, help="static slots (-1: one per CU, 0: one WG per tile)")
     ap.add_argument("--kv-chunk", type=int, default=0,
