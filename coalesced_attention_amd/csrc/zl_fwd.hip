@@ -24,9 +24,10 @@
 //     score registers converted to bf16), so the rescale factor of a query
 //     multiplies registers of the same lane.
 //   - K/V tiles of 64 keys go from HBM straight into LDS with buffer loads
-//     (no staging registers), three stages each, K three blocks ahead of
-//     its use and V two; each wave works on three blocks at once (see the
-//     iteration below) and the workgroup meets one barrier per block.
+//     (no staging registers), four stages each, K and V issued three
+//     iterations before the barrier that publishes them; each wave works on
+//     three blocks at once (see the iteration below) and the workgroup meets
+//     one barrier per block.
 //   - the running max is only raised when a row's new maximum exceeds the
 //     one in use by more than 2^8 (in exp2 units): the probabilities are
 //     then at most 256, the final O / l and LSE are unchanged in exact
@@ -64,8 +65,20 @@ struct Fwd {
   static constexpr int kGroupBytes = 1024 + 16 * kG;
   static constexpr int kGroups = kBN / kG;
   static constexpr int kTileBytes = kGroups * kGroupBytes;
-  static constexpr int kStages = 3;
-  static constexpr int kLdsBytes = 2 * kStages * kTileBytes;
+  // LDS stages and load distances (in key blocks). Iteration j reads K(j+1)
+  // and V(j-1) and issues K(j + kKAhead) and V(j + kVAhead); a stage may be
+  // refilled once the barrier after its last reader has passed: K(x) is last
+  // read in iteration x-1 and V(x) in iteration x+1.
+  static constexpr int kKStages = 4;
+  static constexpr int kVStages = 4;
+  static constexpr int kKAhead = 4;
+  static constexpr int kVAhead = 2;
+  static_assert(kKAhead <= kKStages && kVAhead <= kVStages - 2, "stage reuse distance");
+  // The bottom of iteration j needs K(j+2) and V(j), both issued in iteration
+  // j-2: the loads of iterations j-1 and j (four tiles) may still be in flight.
+  static constexpr int kTilesInFlight = 4;
+  static_assert(kKAhead == 4 && kVAhead == 2, "kTilesInFlight assumes these distances");
+  static constexpr int kLdsBytes = (kKStages + kVStages) * kTileBytes;
   static constexpr int kGroupsPerWave = (kGroups + kWaves - 1) / kWaves;
   static_assert(kBlockM == kWaves * 32, "one 32-row MFMA block per wave");
   static_assert(kBN % 32 == 0 && (D == 64 || D == 128), "shapes");
@@ -127,8 +140,8 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
     }
   };
   constexpr int kLoadsPerTile = C::kGroupsPerWave;  // per wave, per tensor
-  auto kstage = [&](int blk) { return (blk % C::kStages) * C::kTileBytes; };
-  auto vstage = [&](int blk) { return (C::kStages + (blk + C::kStages) % C::kStages) * C::kTileBytes; };
+  auto kstage = [&](int blk) { return (blk % C::kKStages) * C::kTileBytes; };
+  auto vstage = [&](int blk) { return (C::kKStages + (blk + C::kVStages) % C::kVStages) * C::kTileBytes; };
 
   // ---- per-lane LDS offsets (the rest are compile-time immediates)
   // K fragment (A of S^T): row b*32 + l32, chunk 2*ds + half.
@@ -189,13 +202,13 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
   float o_alpha = 1.f;      // pending rescale of O (see the end of an iteration)
 
   if (nblk > 0) {
-    // ---- prologue: K(0..2), a zero V stage for the empty PV of iteration 0,
-    // V(0); S(0) and its max
-    issue_tile(kbase, kstage(0), 0);
-    issue_tile(kbase, kstage(1), 1);
-    issue_tile(kbase, kstage(2), 2);
+    // ---- prologue: K(0..3), a zero V stage for the empty PV of iteration 0,
+    // V(0..1); S(0) and its max
+#pragma unroll
+    for (int b = 0; b < C::kKAhead; ++b) issue_tile(kbase, kstage(b), b);
     issue_tile(vbase, vstage(-1), -1);
-    issue_tile(vbase, vstage(0), 0);
+#pragma unroll
+    for (int b = 0; b < C::kVAhead; ++b) issue_tile(vbase, vstage(b), b);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 s_a[KB], s_b[KB];
@@ -225,14 +238,14 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
     // issued as 2*KB windows; window w = (b, u) exponentiates the 8 scores
     // that form P(j)'s operand (b, u), runs half of S(j+1)'s MFMAs for key
     // block b, and the PV MFMAs for operand (b, u) of P(j-1), alternating a
-    // dependent S MFMA with an independent PV MFMA. Loads run ahead: K(j+3)
-    // and V(j+1) are issued at the top, and the barrier at the bottom waits
-    // only for the loads of earlier iterations.
+    // dependent S MFMA with an independent PV MFMA. Loads run ahead: K(j+4)
+    // and V(j+2) are issued at the top, and the barrier at the bottom waits
+    // only for the loads of iteration j-2 and earlier.
     const bool ragged = (kv_len % C::kBN) != 0;
     auto iteration = [&](int j, f32x16 (&sc)[KB], f32x16 (&sn)[KB], bf16x8 (&pc)[KB][2],
                          const bf16x8 (&pp)[KB][2]) __attribute__((always_inline)) {
-      issue_tile(kbase, kstage(j + 3), j + 3);
-      issue_tile(vbase, vstage(j + 1), j + 1);
+      issue_tile(kbase, kstage(j + C::kKAhead), j + C::kKAhead);
+      issue_tile(vbase, vstage(j + C::kVAhead), j + C::kVAhead);
       if (ragged && j + 1 == nblk) mask(sc, j);
       const char ZL_LDS* kb = k_base(kstage(j + 1));
       const char ZL_LDS* vb = v_base(vstage(j - 1));
@@ -274,7 +287,8 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
         __builtin_amdgcn_sched_barrier(0);
       }
       mx = fmaxf(mx, max16(sn[KB - 1]));
-      __builtin_amdgcn_s_waitcnt(kWaitLoads + 2 * kLoadsPerTile);  // this iteration's loads may still fly
+      static_assert(C::kTilesInFlight * kLoadsPerTile < 16, "vmcnt immediate");
+      __builtin_amdgcn_s_waitcnt(kWaitLoads + C::kTilesInFlight * kLoadsPerTile);
       __syncthreads();
       // O holds PV(0..j-1) relative to the max used for P(j-1); P(j), added
       // next iteration, is relative to m_use: apply the pending factor.
