@@ -15,11 +15,14 @@
 // key block through device-scope fp32 atomics, and makes dQ deterministic.
 //
 // dq_kernel runs the forward's tiles (up to 256 query rows of one item on one
-// head, 8 waves x 32 rows) with the forward's layout: per 64-key block,
+// head, 8 waves x 32 rows) with the forward's layout (64-key LDS tiles): per
+// 32-key half-block,
 //   S^T = K Q^T, dP^T = V dO^T       (A = K / V rows from LDS, B = Q^T / dO^T
 //                                     held in registers; lane = query)
 //   dS^T = s P^T (dP^T - D)          (in the accumulator registers)
 //   dQ^T += K^T dS^T                 (A = K^T transpose reads, B = dS^T)
+// software-pipelined over the halves: the dS arithmetic of one half runs
+// beside the S / dP MFMAs of the next and the dQ MFMAs of the previous.
 // It also computes D for its rows and stores it for dkdv_kernel.
 //
 // dkdv_kernel: one tile = 128 keys of one item on one head, against all of
@@ -96,8 +99,16 @@ struct BwdQ {
   static constexpr int kGB = 1024 + 16 * kG;
   static constexpr int kGroups = kBN / kG;
   static constexpr int kTileBytes = kGroups * kGB;
-  static constexpr int kStages = 3;
-  static constexpr int kLdsBytes = 2 * kStages * kTileBytes;
+  // The key loop runs over 32-key halves of the 64-key LDS tiles. K(x) is
+  // last read by the dQ of half (x, 1), which runs in half (x+1, 0), and V(x)
+  // by the S, dP of half (x, 1), which run in half (x, 0). The barrier between
+  // the halves of block J publishes block J+1 and issues K(J+3), V(J+3), into
+  // the stages of K(J-1) and V(J).
+  static constexpr int kKStages = 4;
+  static constexpr int kVStages = 3;
+  static constexpr int kAhead = 3;
+  static_assert(kAhead == kKStages - 1 && kAhead == kVStages, "stage reuse distance");
+  static constexpr int kLdsBytes = (kKStages + kVStages) * kTileBytes;
   static constexpr int kGroupsPerWave = (kGroups + kWaves - 1) / kWaves;
   static_assert(zl::kFwdBlockM == kWaves * 32, "forward tiles hold 32 rows per wave");
 };
@@ -129,7 +140,7 @@ __device__ __forceinline__ void dq_tile(const zl_tile& tile, const __bf16* __res
   const float c = scale * kLog2e;
 
   // ---- this lane's query row: Q^T and dO^T fragments (head_dim
-  // [ds*16 + 8*half, +8)), D = rowsum(dO * O) and LSE in exp2 units
+  // [ds*16 + 8*half, +8)), s * D with D = rowsum(dO * O), and LSE in exp2 units
   const int qr = wave * 32 + l32;
   const bool qvalid = qr < tile.q_rows;
   const int64_t row = tile.q_row0 + (qvalid ? qr : 0);
@@ -151,7 +162,8 @@ __device__ __forceinline__ void dq_tile(const zl_tile& tile, const __bf16* __res
       for (int e = 0; e < 4; ++e) dpart = fmaf(float(g[4 + e]), o1[e], dpart);
     }
   }
-  const float drow = qvalid ? swap_halves_sum(dpart) : 0.f;
+  // sD = s * D: dS = s P (dP - D) = P (s dP - sD) is then one fma and a multiply
+  const float drow = qvalid ? scale * swap_halves_sum(dpart) : 0.f;
   const float l2 = qvalid ? LSE[row * H + tile.head] * kLog2e : INFINITY;
   if (qvalid && half == 0) Dws[row * H + tile.head] = drow;
 
@@ -160,11 +172,12 @@ __device__ __forceinline__ void dq_tile(const zl_tile& tile, const __bf16* __res
   const __bf16* kbase = K + tile.kv_row0 * rs + int64_t(tile.head) * D;
   const __bf16* vbase = V + tile.kv_row0 * rs + int64_t(tile.head) * D;
 
-  // ---- direct-to-LDS loads of key block `blk` (rows past kv_len read as 0)
+  // ---- direct-to-LDS loads of key block `blk` (rows past kv_len, and every
+  // row of block -1, read as 0)
   const int ld_lane = (lane % G) * int(rs) * 2 + (lane / G) * 16;
   auto issue_tile = [&](const __bf16* base, int stage_off, int blk) __attribute__((always_inline)) {
-    const int rows = min(C::kBN, max(0, kv_len - blk * C::kBN));
-    const int64_t addr = uniform_i64(reinterpret_cast<int64_t>(base + int64_t(blk) * C::kBN * rs));
+    const int rows = blk < 0 ? 0 : min(C::kBN, max(0, kv_len - blk * C::kBN));
+    const int64_t addr = uniform_i64(reinterpret_cast<int64_t>(base + int64_t(max(blk, 0)) * C::kBN * rs));
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<__bf16*>(addr), 0,
                                                         __builtin_amdgcn_readfirstlane(rows * int(rs) * 2),
                                                         kBufferFlags);
@@ -178,8 +191,8 @@ __device__ __forceinline__ void dq_tile(const zl_tile& tile, const __bf16* __res
     }
   };
   constexpr int kLoadsPerTile = C::kGroupsPerWave;
-  auto kstage = [&](int blk) { return (blk % C::kStages) * C::kTileBytes; };
-  auto vstage = [&](int blk) { return (C::kStages + blk % C::kStages) * C::kTileBytes; };
+  auto kstage = [&](int blk) { return ((blk + C::kKStages) % C::kKStages) * C::kTileBytes; };
+  auto vstage = [&](int blk) { return (C::kKStages + blk % C::kVStages) * C::kTileBytes; };
 
   // row fragment (A of S^T and dP^T): row b*32 + l32, chunk 2*ds + half
   const int r_lane = (l32 / G) * GB + (half * G + l32 % G) * 16;
@@ -206,58 +219,105 @@ __device__ __forceinline__ void dq_tile(const zl_tile& tile, const __bf16* __res
   for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
 
   if (nblk > 0) {
-    issue_tile(kbase, kstage(0), 0);
-    issue_tile(vbase, vstage(0), 0);
-    issue_tile(kbase, kstage(1), 1);
-    issue_tile(vbase, vstage(1), 1);
-  }
-  for (int j = 0; j < nblk; ++j) {
-    // K(j), V(j) are older than the two loads of block j + 1
-    __builtin_amdgcn_s_waitcnt(kWaitLoads + 2 * kLoadsPerTile);
-    lds_barrier();  // every wave's part of block j has landed; block j - 1 is no longer read
-    issue_tile(kbase, kstage(j + 2), j + 2);
-    issue_tile(vbase, vstage(j + 2), j + 2);
-    const char ZL_LDS* kr = opaque(kstage(j) + r_lane);
-    const char ZL_LDS* vr = opaque(vstage(j) + r_lane);
-    const char ZL_LDS* kt = opaque(kstage(j) + t_lane);
-
-    // S^T and dP^T: lane = query, register r = key b*32 + 8(r/4) + 4*half + r%4
-    f32x16 s[KB], dp[KB];
+    // ---- software pipeline over 32-key halves t = 2J + h of the key blocks.
+    // Half t computes, in two windows of 16 keys each,
+    //   dS(t) from S(t), dP(t)                          (VALU)
+    //   S(t+1) = K Q^T, dP(t+1) = V dO^T                 (MFMA, K/V rows)
+    //   dQ^T += K(t-1)^T dS(t-1)                         (MFMA, K transpose reads)
+    // so the exponentials of one half run beside the MFMAs of its neighbours.
+    // The prologue loads a zero block -1 for the empty dQ of half 0.
+    issue_tile(kbase, kstage(-1), -1);
 #pragma unroll
-    for (int b = 0; b < KB; ++b) {
-      s[b] = f32x16{};
-      dp[b] = f32x16{};
+    for (int b = 0; b < C::kAhead; ++b) {
+      issue_tile(kbase, kstage(b), b);
+      issue_tile(vbase, vstage(b), b);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLoads + 4 * kLoadsPerTile);  // K(-1), K(0), V(0) landed
+    lds_barrier();
+    f32x16 s_a = f32x16{}, d_a = f32x16{}, s_b, d_b;
+    bf16x8 x_a[2], x_b[2] = {bf16x8{}, bf16x8{}};
+    {
+      const char ZL_LDS* kr = opaque(kstage(0) + r_lane);
+      const char ZL_LDS* vr = opaque(vstage(0) + r_lane);
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row(kr, b, ds), qf[ds], s[b], 0, 0, 0);
-        dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row(vr, b, ds), gf[ds], dp[b], 0, 0, 0);
+        s_a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row(kr, 0, ds), qf[ds], s_a, 0, 0, 0);
+        d_a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row(vr, 0, ds), gf[ds], d_a, 0, 0, 0);
       }
     }
-    const bool last_ragged = j + 1 == nblk && (kv_len % C::kBN) != 0;
-    // dS^T in bf16; k-slot e of operand (b, u) is key b*32 + 16u + 8(e/4) + 4*half + e%4
-    bf16x8 dsb[KB][2];
+    const bool ragged = (kv_len % C::kBN) != 0;
+    // half (J, h): S(t), dP(t) in sc, dc; S(t+1), dP(t+1) into sn, dn; dS(t)
+    // into xc; dS(t-1) from xp
+    auto half_step = [&](int J, int h, const f32x16& sc, const f32x16& dc, f32x16& sn, f32x16& dn,
+                         bf16x8 (&xc)[2], const bf16x8 (&xp)[2]) __attribute__((always_inline)) {
+      const int jn = h ? J + 1 : J, bn = h ? 0 : 1;  // block and half of t+1
+      const int jp = h ? J : J - 1, bp = h ? 0 : 1;  // block and half of t-1
+      const char ZL_LDS* kr = opaque(kstage(jn) + r_lane);
+      const char ZL_LDS* vr = opaque(vstage(jn) + r_lane);
+      const char ZL_LDS* kt = opaque(kstage(jp) + t_lane);
+      const bool mask = ragged && J + 1 == nblk;
+      // four windows (u, q): elements 4q..4q+3 of operand u, a quarter of
+      // the S / dP d-steps and half of the dQ column blocks each
 #pragma unroll
-    for (int b = 0; b < KB; ++b)
+      for (int u = 0; u < 2; ++u) {
+        u32x4 packed;
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+        for (int q = 0; q < 2; ++q) {
+          constexpr int NS = DS / 4, NQ = DB / 2;
+          bf16x8 kf[NS], vf[NS], tf[NQ];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * u + e;
-          float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -l2));
-          if (last_ragged) {
-            const int key = j * C::kBN + b * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key >= kv_len) p = 0.f;
+          for (int i = 0; i < NS; ++i) {
+            kf[i] = read_row(kr, bn, u * (DS / 2) + q * NS + i);
+            vf[i] = read_row(vr, bn, u * (DS / 2) + q * NS + i);
           }
-          dsb[b][u][e] = (__bf16)((dp[b][r] - drow) * (p * scale));
+#pragma unroll
+          for (int i = 0; i < NQ; ++i) tf[i] = read_tr(kt, bp, u, q * NQ + i);
+          // k-slot e of operand u is key 32h + 16u + 8(e/4) + 4*half + e%4
+          float ds4[4];
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int r = 8 * u + 4 * q + e4;
+            float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -l2));
+            if (mask) {
+              const int key = J * C::kBN + h * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+              if (key >= kv_len) p = 0.f;
+            }
+            ds4[e4] = fmaf(dc[r], scale, -drow) * p;
+          }
+          packed[2 * q] = pack_bf16x2(ds4[0], ds4[1]);
+          packed[2 * q + 1] = pack_bf16x2(ds4[2], ds4[3]);
+          pin(packed[2 * q]);
+          pin(packed[2 * q + 1]);
+#pragma unroll
+          for (int i = 0; i < NS; ++i) {
+            const int ds = u * (DS / 2) + q * NS + i;
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[ds], ds == 0 ? f32x16{} : sn, 0, 0, 0);
+            dn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], gf[ds], ds == 0 ? f32x16{} : dn, 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < NQ; ++i)
+            dq[q * NQ + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], xp[u], dq[q * NQ + i], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-    // dQ^T += K^T dS^T
+        xc[u] = __builtin_bit_cast(bf16x8, packed);
+      }
+    };
+    for (int J = 0; J < nblk; ++J) {
+      half_step(J, 0, s_a, d_a, s_b, d_b, x_a, x_b);
+      // K(J+1), V(J+1) landed: only the two loads of the previous barrier may fly
+      __builtin_amdgcn_s_waitcnt(kWaitLoads + 2 * kLoadsPerTile);
+      lds_barrier();
+      issue_tile(kbase, kstage(J + C::kAhead), J + C::kAhead);
+      issue_tile(vbase, vstage(J + C::kAhead), J + C::kAhead);
+      half_step(J, 1, s_b, d_b, s_a, d_a, x_b, x_a);
+    }
+    // ---- drain: dQ^T += K(nblk-1, half 1)^T dS
+    const char ZL_LDS* kt = opaque(kstage(nblk - 1) + t_lane);
 #pragma unroll
-    for (int b = 0; b < KB; ++b)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(kt, b, u, db), dsb[b][u], dq[db], 0, 0, 0);
+      for (int db = 0; db < DB; ++db)
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(kt, 1, u, db), x_b[u], dq[db], 0, 0, 0);
   }
 
   // ---- dQ += dQ^T (lane = query, register r = d db*32 + 8(r/4) + 4*half + r%4);
@@ -409,7 +469,6 @@ __device__ __forceinline__ void dkdv_tile(const zl_tile& tile, const __bf16* __r
       }
     }
     const float c = scale * kLog2e;
-    const bool ragged_keys = tile.kv_len < C::kBN;
     // row reads (A of S and dP): row l32, chunk 2*ds + half
     const int a_lane = (l32 / G) * GB + (half * G + l32 % G) * 16;
     for (int j = 0; j <= nsteps; ++j) {
@@ -436,10 +495,11 @@ __device__ __forceinline__ void dkdv_tile(const zl_tile& tile, const __bf16* __r
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse[e] * kLog2e));
-            if (ragged_keys && !kvalid) p = 0.f;
+            // keys at or past kv_len have zero K / V rows; their P and dS
+            // only reach dV / dK columns of those keys, which are not stored
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse[e] * kLog2e));
             pf[r >> 3][r & 7] = (__bf16)p;
-            sf[r >> 3][r & 7] = (__bf16)((dp[r] - dd[e]) * (p * scale));
+            sf[r >> 3][r & 7] = (__bf16)(fmaf(dp[r], scale, -dd[e]) * p);
           }
         }
 #pragma unroll

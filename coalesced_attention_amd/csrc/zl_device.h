@@ -16,6 +16,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define ZL_LDS __attribute__((address_space(3)))
 
@@ -57,6 +59,12 @@ __device__ __forceinline__ void lds_barrier() {
 template <typename T>
 __device__ __forceinline__ void pin(const T& x) {
   asm volatile("" ::"v"(x));
+}
+
+// Two floats rounded to bf16 (RNE) in one dword, a in the low half.
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(unsigned, v);
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const char ZL_LDS* p) {

@@ -244,7 +244,8 @@ int zl_merge_partials(int32_t n_parts, int64_t rows, int32_t num_heads, int32_t 
  * FlashAttention [7]; the split of the dK / dV work over key/value blocks
  * follows the theta k axis, "What carries the argument"). For every item and
  * head, with P = exp(scale * q K^T - LSE):
- *   D    = rowsum(dO * O)                 (written to d_ws, [q_rows, H] fp32)
+ *   D    = rowsum(dO * O)                 (scale * D is written to d_ws,
+ *                                          [q_rows, H] fp32)
  *   dV  += P^T dO,   dS = P * (dO V^T - D)
  *   dQ  += scale * dS K,   dK += scale * dS^T Q
  * dq [q_rows, H, d], dk and dv [kv_rows, H, d] are fp32 and ACCUMULATED
