@@ -188,6 +188,7 @@ def test_fwd_and_merge_reject_bad_arguments_before_any_hip_call():
     assert m(2, 10, 4, 0, 4, 96, p, p, 10, p, p, None) == -2
     assert m(2, 10, 4, 2, 3, 128, p, p, 10, p, p, None) == -3
     assert m(0, 10, 4, 0, 4, 128, p, p, 10, p, p, None) == -9
+    assert m(65, 10, 4, 0, 4, 128, p, p, 10, p, p, None) == -9   # more than 64 parts
     assert m(2, 10, 4, 0, 4, 128, p, p, 5, p, p, None) == -9   # stride < rows
     assert m(2, 10, 4, 0, 4, 128, p + 4, p, 10, p, p, None) == -6
     q = 1 << 30

@@ -103,7 +103,9 @@ def test_merge_parity(c):
 def test_merge_kernel_against_oracle_merge():
     from coalesced_attention_amd import zl
     rng = np.random.default_rng(3)
-    for d, n_parts, rows, H, h0, hc in [(128, 2, 300, 5, 1, 3), (64, 3, 77, 2, 0, 2), (128, 5, 16, 24, 4, 12)]:
+    # the last case is the largest part count the entry point accepts
+    for d, n_parts, rows, H, h0, hc in [(128, 2, 300, 5, 1, 3), (64, 3, 77, 2, 0, 2), (128, 5, 16, 24, 4, 12),
+                                        (64, 64, 7, 2, 0, 2)]:
         stride = rows + 9
         T = (n_parts - 1) * stride + rows + 4
         o = rng.standard_normal((T, H, d)).astype(np.float32)
