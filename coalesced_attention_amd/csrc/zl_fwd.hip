@@ -24,10 +24,9 @@
 //     score registers converted to bf16), so the rescale factor of a query
 //     multiplies registers of the same lane.
 //   - K/V tiles of 64 keys go from HBM straight into LDS with buffer loads
-//     (no staging registers), four stages each, K and V issued three
-//     iterations before the barrier that publishes them; each wave works on
-//     three blocks at once (see the iteration below) and the workgroup meets
-//     one barrier per block.
+//     (no staging registers), four stages each, K three blocks ahead of
+//     its use and V one; each wave works on three blocks at once (see the
+//     iteration below) and the workgroup meets one barrier per two blocks.
 //   - the running max is only raised when a row's new maximum exceeds the
 //     one in use by more than 2^8 (in exp2 units): the probabilities are
 //     then at most 256, the final O / l and LSE are unchanged in exact
@@ -66,18 +65,18 @@ struct Fwd {
   static constexpr int kGroups = kBN / kG;
   static constexpr int kTileBytes = kGroups * kGroupBytes;
   // LDS stages and load distances (in key blocks). Iteration j reads K(j+1)
-  // and V(j-1) and issues K(j + kKAhead) and V(j + kVAhead); a stage may be
-  // refilled once the barrier after its last reader has passed: K(x) is last
-  // read in iteration x-1 and V(x) in iteration x+1.
+  // and V(j-1) and issues K(j + kKAhead) and V(j + kVAhead). The workgroup
+  // meets a barrier after every odd iteration (and after the last one); it
+  // waits for every load issued so far and publishes K and V for the next
+  // two iterations. A stage may be refilled once a barrier after its last
+  // reader has passed: K(x) is last read in iteration x-1 and V(x) in
+  // iteration x+1, and an even iteration's last barrier lies two iterations
+  // back.
   static constexpr int kKStages = 4;
   static constexpr int kVStages = 4;
-  static constexpr int kKAhead = 4;
-  static constexpr int kVAhead = 2;
-  static_assert(kKAhead <= kKStages && kVAhead <= kVStages - 2, "stage reuse distance");
-  // The bottom of iteration j needs K(j+2) and V(j), both issued in iteration
-  // j-2: the loads of iterations j-1 and j (four tiles) may still be in flight.
-  static constexpr int kTilesInFlight = 4;
-  static_assert(kKAhead == 4 && kVAhead == 2, "kTilesInFlight assumes these distances");
+  static constexpr int kKAhead = 3;
+  static constexpr int kVAhead = 1;
+  static_assert(kKAhead <= kKStages - 1 && kVAhead <= kVStages - 3, "stage reuse distance");
   static constexpr int kLdsBytes = (kKStages + kVStages) * kTileBytes;
   static constexpr int kGroupsPerWave = (kGroups + kWaves - 1) / kWaves;
   static_assert(kBlockM == kWaves * 32, "one 32-row MFMA block per wave");
@@ -202,8 +201,8 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
   float o_alpha = 1.f;      // pending rescale of O (see the end of an iteration)
 
   if (nblk > 0) {
-    // ---- prologue: K(0..3), a zero V stage for the empty PV of iteration 0,
-    // V(0..1); S(0) and its max
+    // ---- prologue: K(0..2), a zero V stage for the empty PV of iteration 0,
+    // V(0); S(0) and its max
 #pragma unroll
     for (int b = 0; b < C::kKAhead; ++b) issue_tile(kbase, kstage(b), b);
     issue_tile(vbase, vstage(-1), -1);
@@ -238,12 +237,12 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
     // issued as 2*KB windows; window w = (b, u) exponentiates the 8 scores
     // that form P(j)'s operand (b, u), runs half of S(j+1)'s MFMAs for key
     // block b, and the PV MFMAs for operand (b, u) of P(j-1), alternating a
-    // dependent S MFMA with an independent PV MFMA. Loads run ahead: K(j+4)
-    // and V(j+2) are issued at the top, and the barrier at the bottom waits
-    // only for the loads of iteration j-2 and earlier.
+    // dependent S MFMA with an independent PV MFMA. Loads run ahead: K(j+3)
+    // and V(j+1) are issued at the top; the barrier at the bottom of every
+    // odd iteration publishes them for the next two iterations.
     const bool ragged = (kv_len % C::kBN) != 0;
     auto iteration = [&](int j, f32x16 (&sc)[KB], f32x16 (&sn)[KB], bf16x8 (&pc)[KB][2],
-                         const bf16x8 (&pp)[KB][2]) __attribute__((always_inline)) {
+                         const bf16x8 (&pp)[KB][2], bool bar) __attribute__((always_inline)) {
       issue_tile(kbase, kstage(j + C::kKAhead), j + C::kKAhead);
       issue_tile(vbase, vstage(j + C::kVAhead), j + C::kVAhead);
       if (ragged && j + 1 == nblk) mask(sc, j);
@@ -287,9 +286,7 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
         __builtin_amdgcn_sched_barrier(0);
       }
       mx = fmaxf(mx, max16(sn[KB - 1]));
-      static_assert(C::kTilesInFlight * kLoadsPerTile < 16, "vmcnt immediate");
-      __builtin_amdgcn_s_waitcnt(kWaitLoads + C::kTilesInFlight * kLoadsPerTile);
-      __syncthreads();
+      if (bar) __syncthreads();
       // O holds PV(0..j-1) relative to the max used for P(j-1); P(j), added
       // next iteration, is relative to m_use: apply the pending factor.
       if (__builtin_amdgcn_ballot_w64(o_alpha != 1.f) != 0) {
@@ -310,10 +307,10 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
     };
     int j = 0;
     for (; j + 1 < nblk; j += 2) {
-      iteration(j, s_a, s_b, p_a, p_b);
-      iteration(j + 1, s_b, s_a, p_b, p_a);
+      iteration(j, s_a, s_b, p_a, p_b, false);
+      iteration(j + 1, s_b, s_a, p_b, p_a, true);
     }
-    if (j < nblk) iteration(j, s_a, s_b, p_a, p_b);
+    if (j < nblk) iteration(j, s_a, s_b, p_a, p_b, true);
     // ---- drain: O += V(nblk-1)^T P(nblk-1)^T
     const bf16x8 (&pl)[KB][2] = (nblk & 1) ? p_a : p_b;
     const char ZL_LDS* vb = v_base(vstage(nblk - 1));
