@@ -202,14 +202,16 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
 
   if (nblk > 0) {
     // ---- prologue: K(0..2), a zero V stage for the empty PV of iteration 0,
-    // V(0); S(0) and its max
-#pragma unroll
-    for (int b = 0; b < C::kKAhead; ++b) issue_tile(kbase, kstage(b), b);
+    // V(0); S(0) and its max. Only K(0) is waited for before S(0); the other
+    // loads land while its MFMAs run.
+    static_assert(C::kKAhead == 3 && C::kVAhead == 1, "prologue load order");
+    issue_tile(kbase, kstage(0), 0);
     issue_tile(vbase, vstage(-1), -1);
-#pragma unroll
-    for (int b = 0; b < C::kVAhead; ++b) issue_tile(vbase, vstage(b), b);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    issue_tile(kbase, kstage(1), 1);
+    issue_tile(vbase, vstage(0), 0);
+    issue_tile(kbase, kstage(2), 2);
+    __builtin_amdgcn_s_waitcnt(kWaitLoads + 4 * kLoadsPerTile);  // K(0) landed
+    lds_barrier();
     f32x16 s_a[KB], s_b[KB];
     bf16x8 p_a[KB][2], p_b[KB][2];
 #pragma unroll
@@ -228,7 +230,7 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
       for (int b = 1; b < KB; ++b) mx = fmaxf(mx, max16(s_a[b]));
       m_use = swap_halves_max(mx) * c;
     }
-    __syncthreads();  // K stage 0 is refilled by the first iteration
+    __syncthreads();  // the prologue's loads land; K stage 0 is refilled in iteration 1
 
     // ---- iteration j, three blocks in flight:
     //   exponentials, row sums and bf16 packing of S(j) -> P(j)     (VALU)
