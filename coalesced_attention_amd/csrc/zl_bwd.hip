@@ -92,7 +92,6 @@ struct BwdQ {
   static constexpr int kWaves = zl::kFwdWaves;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kBN = 64;
-  static constexpr int kKB = kBN / 32;
   static constexpr int kDS = D / 16;
   static constexpr int kDB = D / 32;
   static constexpr int kG = 512 / D;
@@ -130,7 +129,7 @@ __device__ __forceinline__ void dq_tile(const zl_tile& tile, const __bf16* __res
                                         float* __restrict__ dQ, int H, float scale,
                                         char ZL_LDS* smem) {
   using C = BwdQ<D>;
-  constexpr int KB = C::kKB, DS = C::kDS, DB = C::kDB, G = C::kG, GB = C::kGB;
+  constexpr int DS = C::kDS, DB = C::kDB, G = C::kG, GB = C::kGB;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
