@@ -305,3 +305,31 @@ def test_maximum_key_range_and_offsets_past_2gb():
     st = oracle_compare(Stats(), items, Qh, Kh, Vh, O, LSE, 1 / math.sqrt(d), full_limit=64,
                         seed=9)
     st.assert_gates("2^20-key item forward")
+
+
+def test_uncovered_rows_and_empty_worklists_are_left_untouched():
+    """Rows no item covers keep what the caller's buffers held; an empty
+    worklist launches nothing, forward and backward."""
+    from coalesced_attention_amd import zl
+    H, d = 3, 128
+    g = torch.Generator(device="cuda").manual_seed(21)
+    q = torch.randn((300, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((200, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((200, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    sentinel = 7.25
+    for items in ([], [W.Item(40, 100, 10, 150, 1, 2)]):
+        wl = zl.build_worklist(items, 300, 200, H, d, device=q.device)
+        o = torch.full((300, H, d), sentinel, device="cuda")
+        lse = torch.full((300, H), sentinel, device="cuda")
+        zl.coalesced_attn_fwd(wl, q, k, v, o, lse)
+        dq, dk, dv = zl.coalesced_attn_bwd(wl, q, k, v, o, lse, q)
+        torch.cuda.synchronize()
+        covered = torch.zeros((300, H), dtype=torch.bool, device="cuda")
+        for it in items:
+            covered[it.q_off:it.q_off + it.q_len, it.head_begin:it.head_begin + it.head_cnt] = True
+        assert torch.all(o[~covered] == sentinel) and torch.all(lse[~covered] == sentinel)
+        assert torch.all(dq[~covered] == 0)
+        if items:
+            assert torch.isfinite(o[covered]).all() and torch.isfinite(lse[covered]).all()
+        else:
+            assert not dk.any() and not dv.any()
