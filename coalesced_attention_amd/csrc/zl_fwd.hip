@@ -27,10 +27,11 @@
 //     (no staging registers), four stages each, K three blocks ahead of
 //     its use and V one; each wave works on three blocks at once (see the
 //     iteration below) and the workgroup meets one barrier per two blocks.
-//   - the running max is only raised when a row's new maximum exceeds the
-//     one in use by more than 2^8 (in exp2 units): the probabilities are
-//     then at most 256, the final O / l and LSE are unchanged in exact
-//     arithmetic, and most blocks skip the O rescale.
+//   - the shift of a row's exponentials is the maximum of its first key
+//     block, and it is raised only when a lane's running sum of weights
+//     passes 2^32 (or overflows): weights above 1 are exact in floating
+//     point and cancel in O / l and LSE, so the key loop computes no block
+//     maxima; the rare raise recomputes the block from its scores.
 
 #include <hip/hip_runtime.h>
 
@@ -44,7 +45,8 @@ namespace {
 
 using namespace zl::dev;
 
-constexpr float kRescaleSlack = 8.0f;  // log2 units
+// Bound on a lane's running sum of weights before the shift is raised.
+constexpr float kSumLimit = 4294967296.0f;  // 2^32
 
 template <int D>
 struct Fwd {
@@ -123,12 +125,17 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
   // item (and every row of a block outside [0, nblk)) arrive as zeros.
   // Lane l of a group load carries row (l % G), chunk (l / G) of the group.
   const int ld_lane = (lane % G) * int(rs) * 2 + (lane / G) * 16;
+  const int row_bytes = __builtin_amdgcn_readfirstlane(int(rs) * 2);
   auto issue_tile = [&](const __bf16* base, int stage_off, int blk) __attribute__((always_inline)) {
-    const int rows = blk < 0 ? 0 : min(C::kBN, max(0, kv_len - blk * C::kBN));
+    // keys of the block inside the item, on the scalar unit: the opaque
+    // step keeps the clamp from becoming a vector med3
+    int rows = kv_len - blk * C::kBN;
+    rows = rows < C::kBN ? rows : C::kBN;
+    asm volatile("" : "+s"(rows));
+    rows = (blk < 0 || rows < 0) ? 0 : rows;
     const int64_t addr = uniform_i64(reinterpret_cast<int64_t>(base + int64_t(max(blk, 0)) * C::kBN * rs));
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<__bf16*>(addr), 0,
-                                                        __builtin_amdgcn_readfirstlane(rows * int(rs) * 2),
-                                                        kBufferFlags);
+                                                        rows * row_bytes, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < C::kGroupsPerWave; ++i) {
       const int gi = wave * C::kGroupsPerWave + i;
@@ -185,12 +192,16 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
         if (key >= kv_len) s[b][r] = -INFINITY;
       }
   };
-  auto max16 = [&](const f32x16& t) __attribute__((always_inline)) {
-    const float a = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
-    const float b = fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7]));
-    const float d = fmaxf(fmaxf(t[8], t[9]), fmaxf(t[10], t[11]));
-    const float e = fmaxf(fmaxf(t[12], t[13]), fmaxf(t[14], t[15]));
-    return fmaxf(fmaxf(a, b), fmaxf(d, e));
+  // max of 16 scores and a running value as a tree of three-input maxima
+  // (8 v_max3_f32)
+  auto max3 = [](float a, float b, float d) __attribute__((always_inline)) { return fmaxf(fmaxf(a, b), d); };
+  auto max16 = [&](const f32x16& t, float run) __attribute__((always_inline)) {
+    const float a = max3(t[0], t[1], t[2]);
+    const float b = max3(t[3], t[4], t[5]);
+    const float d = max3(t[6], t[7], t[8]);
+    const float e = max3(t[9], t[10], t[11]);
+    const float f = max3(t[12], t[13], t[14]);
+    return max3(max3(a, b, d), max3(e, f, t[15]), run);
   };
 
   f32x16 oacc[DB];
@@ -198,7 +209,6 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
   float m_use = -INFINITY;  // max in use for the block being exponentiated (exp2 units)
   float l_part = 0.f;       // this lane's partial row sum, relative to m_use
-  float o_alpha = 1.f;      // pending rescale of O (see the end of an iteration)
 
   if (nblk > 0) {
     // ---- prologue: K(0..2), a zero V stage for the empty PV of iteration 0,
@@ -225,9 +235,9 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
     }
     if (nblk == 1) mask(s_a, 0);
     {
-      float mx = max16(s_a[0]);
+      float mx = max16(s_a[0], -INFINITY);
 #pragma unroll
-      for (int b = 1; b < KB; ++b) mx = fmaxf(mx, max16(s_a[b]));
+      for (int b = 1; b < KB; ++b) mx = max16(s_a[b], mx);
       m_use = swap_halves_max(mx) * c;
     }
     __syncthreads();  // the prologue's loads land; K stage 0 is refilled in iteration 1
@@ -250,7 +260,7 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
       if (ragged && j + 1 == nblk) mask(sc, j);
       const char ZL_LDS* kb = k_base(kstage(j + 1));
       const char ZL_LDS* vb = v_base(vstage(j - 1));
-      float mx = -INFINITY;
+      const float l_prev = l_part;
 #pragma unroll
       for (int w = 0; w < 2 * KB; ++w) {
         const int b = w / 2, u = w % 2;
@@ -272,10 +282,6 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
         // barrier where nothing overlaps them
         pin(pc[b][u]);
         pin(l_part);
-        if (b > 0 && u == 0) {
-          mx = fmaxf(mx, max16(sn[b - 1]));  // its MFMAs ran in the previous windows
-          pin(mx);
-        }
 #pragma unroll
         for (int i = 0; i < DS / 2; ++i) {
           const int ds = u * (DS / 2) + i;
@@ -287,24 +293,34 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pp[b][u], oacc[db], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      mx = fmaxf(mx, max16(sn[KB - 1]));
       if (bar) __syncthreads();
-      // O holds PV(0..j-1) relative to the max used for P(j-1); P(j), added
-      // next iteration, is relative to m_use: apply the pending factor.
-      if (__builtin_amdgcn_ballot_w64(o_alpha != 1.f) != 0) {
+      // P(j) was taken relative to m_use. Weights above 1 are exact in
+      // floating point, so the shift only has to keep exp2 and the sums far
+      // from overflow: a lane whose running sum left [0, 2^32] (or became
+      // inf) sends its wave down this rare path, which shifts each row by the
+      // maximum of its block and redoes P(j) from the scores, still in
+      // registers. O, which holds P(0..j-1), and l are scaled to match.
+      if (__builtin_amdgcn_ballot_w64(!(l_part <= kSumLimit)) != 0) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < DB; ++i) oacc[i] *= o_alpha;
-      }
-      o_alpha = 1.f;
-      if (j + 1 < nblk) {
-        // Raise the max in use only when a row grew past the slack; l is
-        // rescaled now (it already holds P(j)), O after P(j) has been added.
-        const float m_next = swap_halves_max(mx) * c;
-        if (m_next > m_use + kRescaleSlack) {
-          o_alpha = __builtin_amdgcn_exp2f(m_use - m_next);
-          l_part *= o_alpha;
-          m_use = m_next;
-        }
+        for (int b2 = 0; b2 < KB; ++b2) mx = max16(sc[b2], mx);
+        const float m_new = fmaxf(m_use, swap_halves_max(mx) * c);
+        const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
+        float bs = 0.f;
+#pragma unroll
+        for (int b2 = 0; b2 < KB; ++b2)
+#pragma unroll
+          for (int u2 = 0; u2 < 2; ++u2)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float pv = __builtin_amdgcn_exp2f(fmaf(sc[b2][8 * u2 + e], c, -m_new));
+              bs += pv;
+              pc[b2][u2][e] = (__bf16)pv;
+            }
+        l_part = fmaf(l_prev, alpha, bs);
+#pragma unroll
+        for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+        m_use = m_new;
       }
     };
     int j = 0;

@@ -271,6 +271,33 @@ def test_peaky_queries_exercise_the_running_max():
     st.assert_gates("config 0, queries x4")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_score_jumps_past_the_first_block_raise_the_shift(d):
+    """Keys planted in later key blocks whose scores exceed the first block's
+    maximum by about 60 (the running sums pass 2^32) and by over 128 (exp2
+    would overflow in fp32), one of them in the ragged last block: the rows
+    must be redone with a raised shift and still match the oracle."""
+    H = 2
+    items = [W.Item(0, 300, 0, 1000, 0, H)]
+    g = torch.Generator().manual_seed(17)
+    q = torch.randn((300, H, d), generator=g).to(torch.bfloat16)
+    k = torch.randn((1000, H, d), generator=g)
+    v = torch.randn((1000, H, d), generator=g).to(torch.bfloat16)
+    c = math.log2(math.e) / math.sqrt(d)
+    qf = q.float()
+    k[400, 0] = 4.0 * qf[5, 0]       # block 6: about +60 in exp2 units for row 5
+    k[700, 0] = 16.0 * qf[200, 0]    # block 10: past exp2's fp32 range for row 200
+    k[999, 1] = 6.0 * qf[299, 1]     # last block (40 of 64 keys): row 299 of head 1
+    k = k.to(torch.bfloat16)
+    jump = float((qf[200, 0] * k[700, 0].float()).sum()) * c
+    assert jump > 128, jump
+    log(f"score jumps, d={d}: forward on GPU")
+    _, o, lse = run_fwd(items, q.cuda(), k.cuda(), v.cuda(), H, d)
+    st = oracle_compare(Stats(), items, _host(q), _host(k), _host(v), o.cpu().numpy(),
+                        lse.cpu().numpy(), 1 / math.sqrt(d))
+    st.assert_gates(f"score jumps, d={d}")
+
+
 def test_key_permutation_within_an_item():
     wl, inp, (q, k, v) = _workload(1)
     items = wl.items[:3]
