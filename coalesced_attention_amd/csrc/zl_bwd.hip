@@ -112,12 +112,6 @@ struct BwdQ {
   static_assert(zl::kFwdBlockM == kWaves * 32, "forward tiles hold 32 rows per wave");
 };
 
-// Byte offset of the 16-byte chunk holding (row, col) in a group-layout tile
-// with G rows per group, GB bytes per group; col is a multiple of 8.
-__device__ __forceinline__ int grp_off(int row, int col, int G, int GB) {
-  return (row / G) * GB + ((col / 8) * G + row % G) * 16;
-}
-
 // ---------------------------------------------------------------- dQ
 template <int D>
 __device__ __forceinline__ void dq_tile(const zl_tile& tile, const __bf16* __restrict__ Q,
@@ -174,12 +168,17 @@ __device__ __forceinline__ void dq_tile(const zl_tile& tile, const __bf16* __res
   // ---- direct-to-LDS loads of key block `blk` (rows past kv_len, and every
   // row of block -1, read as 0)
   const int ld_lane = (lane % G) * int(rs) * 2 + (lane / G) * 16;
+  const int row_bytes = __builtin_amdgcn_readfirstlane(int(rs) * 2);
   auto issue_tile = [&](const __bf16* base, int stage_off, int blk) __attribute__((always_inline)) {
-    const int rows = blk < 0 ? 0 : min(C::kBN, max(0, kv_len - blk * C::kBN));
+    // keys of the block inside the item, on the scalar unit: the opaque
+    // step keeps the clamp from becoming a vector med3
+    int rows = kv_len - blk * C::kBN;
+    rows = rows < C::kBN ? rows : C::kBN;
+    asm volatile("" : "+s"(rows));
+    rows = (blk < 0 || rows < 0) ? 0 : rows;
     const int64_t addr = uniform_i64(reinterpret_cast<int64_t>(base + int64_t(max(blk, 0)) * C::kBN * rs));
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<__bf16*>(addr), 0,
-                                                        __builtin_amdgcn_readfirstlane(rows * int(rs) * 2),
-                                                        kBufferFlags);
+                                                        rows * row_bytes, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < C::kGroupsPerWave; ++i) {
       const int gi = wave * C::kGroupsPerWave + i;
@@ -247,14 +246,23 @@ __device__ __forceinline__ void dq_tile(const zl_tile& tile, const __bf16* __res
     const bool ragged = (kv_len % C::kBN) != 0;
     // half (J, h): S(t), dP(t) in sc, dc; S(t+1), dP(t+1) into sn, dn; dS(t)
     // into xc; dS(t-1) from xp
-    auto half_step = [&](int J, int h, const f32x16& sc, const f32x16& dc, f32x16& sn, f32x16& dn,
+    auto half_step = [&](int J, int h, f32x16& sc, const f32x16& dc, f32x16& sn, f32x16& dn,
                          bf16x8 (&xc)[2], const bf16x8 (&xp)[2]) __attribute__((always_inline)) {
       const int jn = h ? J + 1 : J, bn = h ? 0 : 1;  // block and half of t+1
       const int jp = h ? J : J - 1, bp = h ? 0 : 1;  // block and half of t-1
       const char ZL_LDS* kr = opaque(kstage(jn) + r_lane);
       const char ZL_LDS* vr = opaque(vstage(jn) + r_lane);
       const char ZL_LDS* kt = opaque(kstage(jp) + t_lane);
-      const bool mask = ragged && J + 1 == nblk;
+      // Keys at or past kv_len (only in the last block) get a score of -inf,
+      // so P = 0 there. Their K rows are zero, but P = exp2(-LSE log2 e)
+      // could still overflow for a row with a very negative LSE.
+      if (ragged && J + 1 == nblk) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = J * C::kBN + h * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key >= kv_len) sc[r] = -INFINITY;
+        }
+      }
       // four windows (u, q): elements 4q..4q+3 of operand u, a quarter of
       // the S / dP d-steps and half of the dQ column blocks each
 #pragma unroll
@@ -276,11 +284,7 @@ __device__ __forceinline__ void dq_tile(const zl_tile& tile, const __bf16* __res
 #pragma unroll
           for (int e4 = 0; e4 < 4; ++e4) {
             const int r = 8 * u + 4 * q + e4;
-            float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -l2));
-            if (mask) {
-              const int key = J * C::kBN + h * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-              if (key >= kv_len) p = 0.f;
-            }
+            const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -l2));
             ds4[e4] = fmaf(dc[r], scale, -drow) * p;
           }
           packed[2 * q] = pack_bf16x2(ds4[0], ds4[1]);
@@ -389,6 +393,7 @@ __device__ __forceinline__ void dkdv_tile(const zl_tile& tile, const __bf16* __r
   // ---- direct-to-LDS loads of step `step`: Q and dO rows (rows at or past
   // the item's end read as zero), and on waves 6 / 7 the LSE / D values
   const int ld_lane = (lane % G) * int(rs) * 2 + (lane / G) * 16;
+  const int l_lane = lane * H * 4;
   auto issue_step = [&](int step) __attribute__((always_inline)) {
     const int slot = step % C::kRing;
     const int valid = tile.q_rows - step * C::kBM;
@@ -416,7 +421,7 @@ __device__ __forceinline__ void dkdv_tile(const zl_tile& tile, const __bf16* __r
       const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<float*>(addr), 0,
                                                           rows * H * 4, kBufferFlags);
       const int off = C::kOffL + slot * C::kLSlot + (is_lse ? 0 : 256);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void ZL_LDS*)(smem + off), 4, lane * H * 4,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void ZL_LDS*)(smem + off), 4, l_lane,
                                                0, 0, 0);
     }
   };
