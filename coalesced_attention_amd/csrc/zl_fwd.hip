@@ -246,10 +246,11 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
     //   exponentials, row sums and bf16 packing of S(j) -> P(j)     (VALU)
     //   S(j+1) = K(j+1) Q^T                                          (MFMA)
     //   O += V(j-1)^T P(j-1)^T                                       (MFMA)
-    // issued as 2*KB windows; window w = (b, u) exponentiates the 8 scores
-    // that form P(j)'s operand (b, u), runs half of S(j+1)'s MFMAs for key
-    // block b, and the PV MFMAs for operand (b, u) of P(j-1), alternating a
-    // dependent S MFMA with an independent PV MFMA. Loads run ahead: K(j+3)
+    // issued as 4*KB windows; the two windows of pair (b, u) each
+    // exponentiate 4 of the 8 scores that form P(j)'s operand (b, u), run a
+    // quarter of S(j+1)'s MFMAs for key block b, and half of the PV MFMAs for
+    // operand (b, u) of P(j-1), alternating a dependent S MFMA with an
+    // independent PV MFMA. Loads run ahead: K(j+3)
     // and V(j+1) are issued at the top; the barrier at the bottom of every
     // odd iteration publishes them for the next two iterations.
     const bool ragged = (kv_len % C::kBN) != 0;
@@ -264,34 +265,37 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
 #pragma unroll
       for (int w = 0; w < 2 * KB; ++w) {
         const int b = w / 2, u = w % 2;
-        bf16x8 kf[DS / 2], vf[DB];
+        u32x4 packed;
+        // two sub-windows of 4 scores, 2 S MFMAs and 2 PV MFMAs each
 #pragma unroll
-        for (int i = 0; i < DS / 2; ++i) kf[i] = read_k(kb, b, u * (DS / 2) + i);
+        for (int hw = 0; hw < 2; ++hw) {
+          constexpr int NS = DS / 4, NV = DB / 2;
+          bf16x8 kf[NS], vf[NV];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vf[db] = read_v(vb, b, u, db);
-        float pe[8];
+          for (int i = 0; i < NS; ++i) kf[i] = read_k(kb, b, u * (DS / 2) + hw * NS + i);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[b][8 * u + e], c, -m_use));
-        // fp32 row sums of the unrounded weights: LSE = m + ln l must not
-        // carry the bf16 rounding of a few dominant weights
-        l_part += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+          for (int i = 0; i < NV; ++i) vf[i] = read_v(vb, b, u, hw * NV + i);
+          float pe[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pc[b][u][e] = (__bf16)pe[e];
-        // keep this window's vector work inside the window: the results are
-        // only read next iteration, and would otherwise be sunk past the
-        // barrier where nothing overlaps them
-        pin(pc[b][u]);
-        pin(l_part);
+          for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[b][8 * u + 4 * hw + e], c, -m_use));
+          l_part += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+          packed[2 * hw] = pack_bf16x2(pe[0], pe[1]);
+          packed[2 * hw + 1] = pack_bf16x2(pe[2], pe[3]);
+          pin(packed[2 * hw]);
+          pin(packed[2 * hw + 1]);
+          pin(l_part);
 #pragma unroll
-        for (int i = 0; i < DS / 2; ++i) {
-          const int ds = u * (DS / 2) + i;
-          sn[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[ds], ds == 0 ? f32x16{} : sn[b], 0, 0, 0);
-          if (i < DB) oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pp[b][u], oacc[i], 0, 0, 0);
+          for (int i = 0; i < NS; ++i) {
+            const int ds = u * (DS / 2) + hw * NS + i;
+            sn[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[ds], ds == 0 ? f32x16{} : sn[b], 0, 0, 0);
+            if (i < NV) oacc[hw * NV + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pp[b][u], oacc[hw * NV + i], 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = NS; i < NV; ++i)
+            oacc[hw * NV + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pp[b][u], oacc[hw * NV + i], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int db = DS / 2; db < DB; ++db)
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pp[b][u], oacc[db], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        pc[b][u] = __builtin_bit_cast(bf16x8, packed);
       }
       if (bar) __syncthreads();
       // P(j) was taken relative to m_use. Weights above 1 are exact in
