@@ -298,6 +298,25 @@ def test_score_jumps_past_the_first_block_raise_the_shift(d):
     st.assert_gates(f"score jumps, d={d}")
 
 
+def test_scores_rising_along_the_keys_raise_the_shift_repeatedly():
+    """Keys drift towards the direction of query row 0, so its scores (and
+    those of rows correlated with it) climb by ~200 in exp2 units over 32
+    key blocks: the running sums pass 2^32 every few blocks and the shift is
+    raised again and again within one tile."""
+    H, d = 1, 128
+    items = [W.Item(0, 96, 0, 2000, 0, H)]
+    g = torch.Generator().manual_seed(23)
+    q = torch.randn((96, H, d), generator=g).to(torch.bfloat16)
+    ramp = torch.linspace(0.0, 12.0, 2000).view(2000, 1, 1)
+    k = (torch.randn((2000, H, d), generator=g) + ramp * q[0].float()).to(torch.bfloat16)
+    v = torch.randn((2000, H, d), generator=g).to(torch.bfloat16)
+    log("rising scores: forward on GPU")
+    _, o, lse = run_fwd(items, q.cuda(), k.cuda(), v.cuda(), H, d)
+    st = oracle_compare(Stats(), items, _host(q), _host(k), _host(v), o.cpu().numpy(),
+                        lse.cpu().numpy(), 1 / math.sqrt(d))
+    st.assert_gates("rising scores")
+
+
 def test_key_permutation_within_an_item():
     wl, inp, (q, k, v) = _workload(1)
     items = wl.items[:3]
