@@ -16,7 +16,6 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
-#include <string>
 #include <vector>
 
 #include "zl.h"
@@ -25,20 +24,20 @@
 namespace zl {
 
 namespace {
-thread_local std::string g_error;
+// fixed storage: reporting an error never allocates, so no exception can
+// leave an entry point through it
+thread_local char g_error[512];
 }
 
 int fail(int code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_error, sizeof g_error, fmt, ap);
   va_end(ap);
-  g_error = buf;
   return code;
 }
 
-void clear_error() { g_error.clear(); }
+void clear_error() { g_error[0] = '\0'; }
 
 int check_worklist(const void* h_wl, const zl_worklist_header** hdr) {
   if (!h_wl) return fail(ZL_ERR_NULL, "host worklist is NULL");
@@ -114,7 +113,7 @@ extern "C" const char* zl_status_string(int status) {
   }
 }
 
-extern "C" const char* zl_last_error(void) { return g_error.c_str(); }
+extern "C" const char* zl_last_error(void) { return g_error; }
 
 namespace {
 
