@@ -238,6 +238,14 @@ def _stream_handle(stream, device) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _check_device(device, **tensors):
+    """Every tensor must live on ``device`` (a GPU): a host or foreign-device
+    pointer handed to a kernel would fault instead of failing."""
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != device):
+            raise ValueError(f"{name} must be a CUDA tensor on {device}, got {t.device}")
+
+
 def _check_qkv(wl: Worklist, q, k, v):
     import torch
     h = wl.header
@@ -247,6 +255,9 @@ def _check_qkv(wl: Worklist, q, k, v):
         if tuple(t.shape) != (rows, h.num_heads, h.head_dim):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, worklist expects "
                              f"{(rows, h.num_heads, h.head_dim)}")
+    _check_device(q.device, k=k, v=v)
+    if wl.device is not None:
+        _check_device(q.device, worklist=wl.device)
 
 
 def coalesced_attn_fwd(wl: Worklist, q, k, v, o=None, lse=None, stream=None, workspace=None):
@@ -268,6 +279,7 @@ def coalesced_attn_fwd(wl: Worklist, q, k, v, o=None, lse=None, stream=None, wor
         raise ValueError("o and lse must be contiguous fp32")
     if tuple(o.shape) != (h.q_rows, h.num_heads, h.head_dim) or tuple(lse.shape) != (h.q_rows, h.num_heads):
         raise ValueError("o / lse shape does not match the worklist")
+    _check_device(q.device, o=o, lse=lse, workspace=workspace)
     ws_ptr = None
     if wl.workspace_floats > 0:
         if workspace is None:
@@ -306,6 +318,7 @@ def coalesced_attn_bwd(wl: Worklist, q, k, v, o, lse, dout, dq=None, dk=None, dv
                            ("ws", ws, (h.q_rows, h.num_heads))):
         if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous fp32 of shape {tuple(shape)}")
+    _check_device(q.device, o=o, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv, ws=ws)
     _check(lib.zl_coalesced_attn_bwd(wl.host_ptr(), wl.device.data_ptr(), q.data_ptr(), k.data_ptr(),
                                      v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
@@ -329,8 +342,10 @@ def merge_partials(o, lse, row0: int, n_parts: int, rows: int, part_row_stride: 
     if lse_out is None:
         lse_out = torch.empty((rows, H), dtype=torch.float32, device=o.device)
     if tuple(o_out.shape) != (rows, H, d) or tuple(lse_out.shape) != (rows, H) \
-            or not o_out.is_contiguous() or not lse_out.is_contiguous():
-        raise ValueError("o_out / lse_out shape mismatch")
+            or not o_out.is_contiguous() or not lse_out.is_contiguous() \
+            or o_out.dtype != torch.float32 or lse_out.dtype != torch.float32:
+        raise ValueError("o_out / lse_out must be contiguous fp32 of shapes [rows, H, d] / [rows, H]")
+    _check_device(o.device, o=o, lse=lse, o_out=o_out, lse_out=lse_out)
     _check(lib.zl_merge_partials(n_parts, rows, H, head_begin, head_cnt, d,
                                  o.data_ptr() + row0 * H * d * 4, lse.data_ptr() + row0 * H * 4,
                                  part_row_stride, o_out.data_ptr(), lse_out.data_ptr(),

@@ -317,6 +317,30 @@ def test_scores_rising_along_the_keys_raise_the_shift_repeatedly():
     st.assert_gates("rising scores")
 
 
+def test_binding_rejects_host_tensors_before_any_launch():
+    """A host tensor among the outputs, gradients or merge buffers raises
+    ValueError in the binding; no pointer of it reaches a kernel."""
+    from coalesced_attention_amd import zl
+    items = [W.Item(0, 64, 0, 64, 0, 2)]
+    q, k, v = (torch.randn((64, 2, 64)).to(torch.bfloat16).cuda() for _ in range(3))
+    wl = zl.build_worklist(items, 64, 64, 2, 64, n_slots=4, device=q.device)
+    with pytest.raises(ValueError):
+        zl.coalesced_attn_fwd(wl, q, k, v, o=torch.zeros((64, 2, 64)))
+    with pytest.raises(ValueError):
+        zl.coalesced_attn_fwd(wl, q, k.cpu(), v)
+    o, lse = zl.coalesced_attn_fwd(wl, q, k, v)
+    with pytest.raises(ValueError):
+        zl.coalesced_attn_bwd(wl, q, k, v, o, lse, torch.zeros((64, 2, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        zl.coalesced_attn_bwd(wl, q, k, v, o, lse, q, dk=torch.zeros((64, 2, 64)))
+    with pytest.raises(ValueError):
+        zl.merge_partials(o, lse, 0, 2, 32, 32, 0, 2, o_out=torch.zeros((32, 2, 64)))
+    with pytest.raises(ValueError):
+        zl.merge_partials(o, lse, 0, 2, 32, 32, 0, 2,
+                          o_out=torch.zeros((32, 2, 64), dtype=torch.float64, device=q.device))
+    torch.cuda.synchronize()
+
+
 def test_key_permutation_within_an_item():
     wl, inp, (q, k, v) = _workload(1)
     items = wl.items[:3]
