@@ -7,7 +7,7 @@
 // Sequence Placement for Mixed Image-Video DiT Training", Abstract; shards
 // per the pith.science review of arXiv 2608.01150, "What carries the
 // argument"). The attention is exact softmax attention computed block by
-// block with a running maximum and sum (the IO-aware exact method the
+// block with a running shift and sum (the IO-aware exact method the
 // review's "Assumptions" section cites as FlashAttention [7]).
 //
 // Work decomposition (per workgroup of 8 waves, two per SIMD, one tile at a
@@ -207,7 +207,7 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
   f32x16 oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m_use = -INFINITY;  // max in use for the block being exponentiated (exp2 units)
+  float m_use = -INFINITY;  // the row's shift (exp2 units): its first block's max, raised on overflow
   float l_part = 0.f;       // this lane's partial row sum, relative to m_use
 
   if (nblk > 0) {
