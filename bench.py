@@ -14,8 +14,14 @@ The other steps of the path are timed beside it in the same run: the
 KV-split merge (two 27450-row partials on 12 heads, reported in GB/s) and
 the recompute-from-LSE backward of the same mix with an upstream gradient
 (reported in TFLOP/s under both flop conventions: 5 GEMMs = 2.5x the
-forward's flops, and 4 GEMMs = 2x). The cpu_baseline leg times the fp64
-oracle on a bounded sample of the same workload on the host cores.
+forward's flops, and 4 GEMMs = 2x). The ``configs`` object times the
+forward on the other workloads (the tiny check, images only, the KV-split
+shard with its merge, with and without the in-launch key split, and the two
+second-workload shares), and ``price_table`` gives the additivity ratios of
+the mixed rank share. Every GPU time comes from HIP events on the launch
+stream; medians and minima are reported beside the means. The cpu_baseline
+leg times the fp64 oracle on a bounded sample of the same workload on the
+host cores (one thread per core, single-threaded BLAS).
 """
 
 from __future__ import annotations
@@ -45,6 +51,9 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config forward records (configs 0, 1, 3, 5, 6)")
+    ap.add_argument("--no-price", action="store_true", help="skip the additivity ratios")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time")
     ap.add_argument("--price-table", action="store_true",
                     help="instead of the bench line: per-(bucket, theta) prices of the workload's items "
@@ -98,50 +107,91 @@ def _events_ms(fn, steps, stream):
     return start.elapsed_time(end) / steps
 
 
+def _launch_ms(fn, steps, stream):
+    """Duration of each of `steps` calls of fn(), from a pair of HIP events
+    around each call on the stream the kernels run on."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+    evs[-1][1].synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def _spread(ms):
+    ms = sorted(ms)
+    return {"ms_mean": round(sum(ms) / len(ms), 4), "ms_median": round(float(np.median(ms)), 4),
+            "ms_min": round(ms[0], 4), "ms_max": round(ms[-1], 4), "launches": len(ms)}
+
+
 def _cpu_baseline(wl, inp, target_s):
-    """The fp64 oracle, as it stands, on a bounded sample of the workload."""
+    """The fp64 oracle, as it stands, on a bounded sample of the workload:
+    one worker thread per host core (at most 16, the share of the host one
+    GPU gets), each running (item, head) units with single-threaded BLAS
+    (numpy releases the interpreter lock inside its array kernels)."""
+    import threading
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
     from oracle.attention import coalesced_forward_rows
     from coalesced_attention_amd.workloads import sample_rows
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    host_cpus = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, host_cpus))
     Qh, Kh, Vh = (x.float().numpy() for x in (inp.q, inp.k, inp.v))
     s = wl.softmax_scale
     d = wl.head_dim
+
     # pass 0: the rows the parity tests check (every row of short items,
     # four per 128-row block of long ones), in a seeded random order of
     # (item, head) units; later passes: fresh seeded rows of the long items;
     # stop once the target time is spent
-    def units_of(pass_no):
-        out = []
-        for idx, it in enumerate(wl.items):
-            if pass_no > 0 and it.q_len <= 1024:
-                continue
-            rows = sample_rows(it, seed=idx + 1000 * pass_no)
-            for h in range(it.head_begin, it.head_begin + it.head_cnt):
-                out.append((it, h, rows))
-        return [out[i] for i in np.random.default_rng(pass_no).permutation(len(out))]
-    flops = 0
-    rows_done = 0
-    passes = 0
+    def units():
+        pass_no = 0
+        while True:
+            out = []
+            for idx, it in enumerate(wl.items):
+                if pass_no > 0 and it.q_len <= 1024:
+                    continue
+                rows = sample_rows(it, seed=idx + 1000 * pass_no)
+                for h in range(it.head_begin, it.head_begin + it.head_cnt):
+                    out.append((pass_no, it, h, rows))
+            for i in np.random.default_rng(pass_no).permutation(len(out)):
+                yield out[i]
+            pass_no += 1
+
+    gen = units()
+    lock = threading.Lock()
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 <= target_s:
-        for it, h, rows in units_of(passes):
+
+    def worker():
+        flops = rows_done = last_pass = 0
+        while True:
+            with lock:
+                if time.perf_counter() - t0 > target_s:
+                    break
+                pass_no, it, h, rows = next(gen)
             coalesced_forward_rows(Qh, Kh, Vh, it, h, rows, s)
             flops += 4 * len(rows) * it.kv_len * d
             rows_done += len(rows)
-            if time.perf_counter() - t0 > target_s:
-                break
-        passes += 1
+            last_pass = max(last_pass, pass_no)
+        return flops, rows_done, last_pass
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+        res = [f.result() for f in [ex.submit(worker) for _ in range(workers)]]
     el = time.perf_counter() - t0
+    flops = sum(r[0] for r in res)
+    rows_done = sum(r[1] for r in res)
+    passes = max(r[2] for r in res) + 1
     total_rows = sum(it.q_len * it.head_cnt for it in wl.items)
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "host_cpus": host_cpus, "blas_threads_per_worker": 1,
             "sample": f"{rows_done} (query row, head) pairs of the same workload ({total_rows} in all): "
                       f"every image row and 4 rows per 128-row block of the video shard, then "
                       f"fresh rows of the shard ({passes} pass(es); {flops / 1e9:.1f} GFLOP in "
-                      f"{el:.1f} s, fp64 numpy)"}
+                      f"{el:.1f} s, fp64 numpy, {workers} worker threads)"}
 
 
 def _bench_backward(zl, W, dev, stream, n_slots):
@@ -173,10 +223,12 @@ def _bench_backward(zl, W, dev, stream, n_slots):
     for _ in range(2):
         bwd()
     torch.cuda.synchronize()
-    ms = _events_ms(bwd, 10, stream)
+    sp = _spread(_launch_ms(bwd, 10, stream))
+    ms = sp["ms_mean"]
     zms = _events_ms(zero, 10, stream)
     F = wl.flops_fwd()
-    return {"workload": wl.name, "ms": round(ms, 4), "zero_grads_ms": round(zms, 4),
+    return {"workload": wl.name, "ms": round(ms, 4), "ms_median": sp["ms_median"], "ms_min": sp["ms_min"],
+            "zero_grads_ms": round(zms, 4),
             "TFLOP/s": round(2.5 * F / (ms * 1e-3) / 1e12, 2),
             "TFLOP/s_4gemm": round(2.0 * F / (ms * 1e-3) / 1e12, 2),
             "pct_of_peak": round(100 * 2.5 * F / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
@@ -228,6 +280,65 @@ def _price_table(zl, wl, q, k, v, dev, n_slots):
             "data": "synthetic"}
 
 
+def _bench_configs(zl, W, dev, stream, n_slots):
+    """Forward time of the other workloads: the tiny check (microseconds),
+    images only, the KV-split shard with its theta-k merge (with and without
+    the in-launch key split), and the two second-workload shares. HIP events
+    around each launch; ~20 launches after 3 warm-ups (fewer on the long
+    ones)."""
+    import torch
+    out = {}
+    for c, kv_chunk in ((0, 0), (1, 0), (3, 0), (3, 27456), (5, 0), (6, 0)):
+        wl = W.config(c)
+        inp = W.make_inputs(wl)
+        q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+        del inp
+        built = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim,
+                                  n_slots=n_slots, kv_chunk=kv_chunk)
+        built.to(dev)
+        o = torch.empty((wl.q_rows, wl.num_heads, wl.head_dim), dtype=torch.float32, device=dev)
+        lse = torch.empty((wl.q_rows, wl.num_heads), dtype=torch.float32, device=dev)
+        ws = (torch.empty(built.workspace_floats, dtype=torch.float32, device=dev)
+              if built.workspace_floats else None)
+
+        def fwd():
+            zl.coalesced_attn_fwd(built, q, k, v, o, lse, stream=stream, workspace=ws)
+
+        for _ in range(3):
+            fwd()
+        torch.cuda.synchronize()
+        probe = _events_ms(fwd, 2, stream)
+        n = max(5, min(20, int(600.0 / max(probe, 1e-3))))
+        sp = _spread(_launch_ms(fwd, n, stream))
+        F = wl.flops_fwd()
+        rec = {"workload": wl.name, "kv_chunk": kv_chunk, "flops": F, "tiles": built.n_tiles, **sp,
+               "TFLOP/s": round(F / (sp["ms_median"] * 1e-3) / 1e12, 2),
+               "frac": round(F / (sp["ms_median"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        if c == 0:
+            rec = {"workload": wl.name, "kv_chunk": kv_chunk, "flops": F, "tiles": built.n_tiles,
+                   "us_median": round(1e3 * sp["ms_median"], 2), "us_min": round(1e3 * sp["ms_min"], 2),
+                   "launches": sp["launches"]}
+        for m in wl.merges:  # the theta-k merge of the partials, after the forward
+            mo = torch.empty((m.rows, wl.num_heads, wl.head_dim), dtype=torch.float32, device=dev)
+            ml = torch.empty((m.rows, wl.num_heads), dtype=torch.float32, device=dev)
+
+            def step():
+                fwd()
+                zl.merge_partials(o, lse, m.row0, m.n_parts, m.rows, m.part_row_stride,
+                                  m.head_begin, m.head_cnt, mo, ml, stream=stream)
+
+            step()
+            torch.cuda.synchronize()
+            spm = _spread(_launch_ms(step, n, stream))
+            if c != 0:
+                rec["with_merge"] = {"ms_median": spm["ms_median"], "ms_min": spm["ms_min"],
+                                     "TFLOP/s": round(F / (spm["ms_median"] * 1e-3) / 1e12, 2)}
+        out[f"{c}" if kv_chunk == 0 else f"{c}_kv_chunk_{kv_chunk}"] = rec
+        del q, k, v, o, lse, ws, built
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     a = _args()
     if a.gpus != 1:
@@ -277,9 +388,11 @@ def main():
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    kern_ms = _events_ms(step, a.steps, stream)
+    launch_ms = _launch_ms(step, a.steps, stream)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    sp = _spread(launch_ms)
+    kern_ms = sp["ms_mean"]
 
     flops = wl.flops_fwd()
     tflops = flops / (ms * 1e-3) / 1e12
@@ -296,12 +409,25 @@ def main():
                    "schedule_makespan_over_mean": round(built.header.max_slot_cost * max(1, n_slots)
                                                         / max(1, built.header.total_cost), 4)},
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "launch_ms": sp,
+        "tflops_at_median": round(flops / (sp["ms_median"] * 1e-3) / 1e12, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("fwd_kernel<128>"), "kernel": "fwd_kernel<128>",
                      "kernel_ms": round(kern_ms, 4)},
         "worklist_build_ms": round(wl_ms, 3),
     }
+    print(f"[bench] headline forward: {sp}", file=sys.stderr, flush=True)
+
+    if not a.no_price and a.config == 2:
+        pt = _price_table(zl, wl, q, k, v, dev, n_slots)
+        out["price_table"] = {k2: pt[k2] for k2 in ("coalesced_ms", "sum_bucket_launches_ms",
+                                                    "sum_single_prices_ms", "coalesced_over_bucket_launches",
+                                                    "coalesced_over_single_prices")}
+        out["price_table"]["buckets"] = [{k2: r[k2] for k2 in ("q_len", "kv_len", "head_cnt", "count",
+                                                               "single_ms", "bucket_ms")}
+                                         for r in pt["buckets"]]
+        print(f"[bench] price table done", file=sys.stderr, flush=True)
 
     if not a.no_merge:
         # KV-split merge at its full size: 2 partials x 27450 rows x 12 of 24 heads
@@ -318,15 +444,23 @@ def main():
         for _ in range(3):
             merge()
         torch.cuda.synchronize()
-        mms = _events_ms(merge, 20, stream)
+        msp = _spread(_launch_ms(merge, 20, stream))
+        mms = msp["ms_mean"]
         mbytes = (parts + 1) * rows * 12 * (d + 1) * 4
         out["merge"] = {"workload": "kv-split merge, 2 x 27450 rows x 12 heads x 128", "ms": round(mms, 4),
+                        "ms_median": msp["ms_median"], "ms_min": msp["ms_min"],
                         "GB/s": round(mbytes / (mms * 1e-3) / 1e9, 1),
                         "frac_of_hbm_peak": round(mbytes / (mms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                         "bytes": mbytes, "traffic": measured_traffic("merge_kernel<128>")}
+        del po, pl, mo, ml
 
     if not a.no_bwd:
         out["backward"] = _bench_backward(zl, W, dev, stream, n_slots)
+        print(f"[bench] backward done", file=sys.stderr, flush=True)
+
+    if not a.no_configs:
+        out["configs"] = _bench_configs(zl, W, dev, stream, n_slots)
+        print(f"[bench] configs done", file=sys.stderr, flush=True)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(wl, inp, a.cpu_seconds)

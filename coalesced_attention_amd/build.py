@@ -1,4 +1,6 @@
-"""Build libzl.so in-tree with hipcc for gfx950.
+"""Build libzl.so in-tree: the HIP kernels with hipcc for gfx950, the host
+half (validation, worklist builder) with the host C++ compiler, linked into
+one shared library.
 
     python -m coalesced_attention_amd.build        # or build() from Python
 
@@ -11,6 +13,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -18,13 +21,20 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libzl.so")
 
-SOURCES = ["zl_host.cpp", "zl_fwd.hip", "zl_merge.hip", "zl_bwd.hip"]
+DEVICE_SOURCES = ["zl_fwd.hip", "zl_merge.hip", "zl_bwd.hip"]
+HOST_SOURCES = ["zl_host.cpp"]
 
-HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+# Flags of the host object. The host code validates floats (a NaN softmax
+# scale must be rejected), so it is built with the default IEEE semantics;
+# the sanitizer test builds the same source with these flags too.
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-function"]
+
+DEVICE_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # inputs carry no NaNs: lets fmaxf map to v_max3 without canonicalizing
+    # the kernels take finite inputs (a documented precondition): lets fmaxf
+    # map to v_max3 without canonicalizing. Kernel files only.
     "-fno-honor-nans",
     # fp32 atomicAdd on device memory as the hardware atomic (no CAS loop)
     "-munsafe-fp-atomics",
@@ -39,21 +49,55 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: libzl.so cannot be built")
 
 
+def host_cxx() -> str:
+    for cand in (os.environ.get("ZL_HOST_CXX"), shutil.which("g++"), shutil.which("c++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler found: libzl.so cannot be built")
+
+
+def _quiet(text: str) -> str:
+    return "\n".join(l for l in text.splitlines()
+                     if "is not a recognized feature for this target" not in l)
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                     if "is not a recognized feature for this target" not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
-    if verbose and msgs.strip():
-        print(msgs, flush=True)
-    os.replace(tmp, LIB)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    with tempfile.TemporaryDirectory(prefix="zl_build_") as tmp:
+        jobs, objs = [], []
+        for s in DEVICE_SOURCES:
+            o = os.path.join(tmp, s + ".o")
+            jobs.append([hipcc(), *DEVICE_FLAGS, *inc, "-c", os.path.join(CSRC, s), "-o", o])
+            objs.append(o)
+        for s in HOST_SOURCES:
+            o = os.path.join(tmp, s + ".o")
+            jobs.append([host_cxx(), *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, s), "-o", o])
+            objs.append(o)
+        procs = []
+        for cmd in jobs:
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                                text=True)))
+        failed = []
+        for cmd, p in procs:
+            out, _ = p.communicate()
+            msgs = _quiet(out)
+            if p.returncode != 0:
+                failed.append(f"{' '.join(cmd)}\n{msgs}")
+            elif verbose and msgs.strip():
+                print(msgs, flush=True)
+        if failed:
+            raise RuntimeError("compilation failed:\n" + "\n\n".join(failed))
+        tmp_lib = LIB + ".tmp"
+        link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        if verbose:
+            print(" ".join(link), flush=True)
+        res = subprocess.run(link, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed ({res.returncode}):\n{_quiet(res.stdout + res.stderr)}")
+    os.replace(tmp_lib, LIB)
     return LIB
 
 

@@ -3,12 +3,11 @@
 // headers, so it builds with hipcc for the library and with g++ (under
 // sanitizers) for host-only checks.
 //
-// Scheduling reading: the engine "stably schedules and fuses" whole
-// sequences and distributed-attention shards on a shared rank (pith.science
-// review of arXiv 2608.01150, "What carries the argument"). Tiles are cut
-// per (item, head, query block), sorted by cost with a total order that
-// keeps equal costs in cut order (a stable sort), and placed longest first
-// on the least-loaded slot.
+// Scheduling reading: the engine places whole sequences and shards on one
+// rank with a stable schedule (pith.science review of arXiv 2608.01150,
+// "What carries the argument"). Tiles are cut per (item, head, query block),
+// sorted by cost with a total order that keeps equal costs in cut order (a
+// stable sort), and placed longest first on the least-loaded slot.
 
 #include <algorithm>
 #include <cmath>
@@ -46,7 +45,8 @@ int check_worklist(const void* h_wl, const zl_worklist_header** hdr) {
   if (h->abi_version != ZL_ABI_VERSION)
     return fail(ZL_ERR_WORKLIST, "worklist built for ABI %u, library is %d", h->abi_version,
                 ZL_ABI_VERSION);
-  if ((h->head_dim != 64 && h->head_dim != 128) || h->num_heads < 1 || h->n_tiles < 0 ||
+  if ((h->head_dim != 64 && h->head_dim != 128) || h->num_heads < 1 ||
+      int64_t(h->num_heads) * h->head_dim > kMaxRowElems || h->n_tiles < 0 ||
       h->n_slots < 0 || h->n_slots > kMaxSlots || h->block_m != kFwdBlockM ||
       !(h->softmax_scale > 0.f) || h->q_rows < 0 || h->kv_rows < 0)
     return fail(ZL_ERR_WORKLIST, "worklist header fields out of range");
@@ -226,6 +226,8 @@ extern "C" int zl_build_worklist(const zl_problem* problem, const zl_item* items
   if ((p.head_dim != 64 && p.head_dim != 128) || p.num_heads < 1 || p.q_rows < 0 ||
       p.kv_rows < 0)
     return fail(ZL_ERR_SHAPE, "head_dim must be 64 or 128 and sizes non-negative");
+  if (int64_t(p.num_heads) * p.head_dim > kMaxRowElems)
+    return fail(ZL_ERR_SHAPE, "num_heads * head_dim exceeds %lld", (long long)kMaxRowElems);
   if (p.kv_chunk < 0) return fail(ZL_ERR_ARG, "problem.kv_chunk must be >= 0");
   if (!(p.softmax_scale <= 0.f || std::isfinite(p.softmax_scale)))
     return fail(ZL_ERR_ARG, "softmax_scale must be finite");

@@ -371,3 +371,20 @@ def sample_rows(item: Item, seed: int, block: int = 128,
         rows += [b0, b1 - 1]
         rows += list(rng.integers(b0, b1, size=2))
     return np.unique(np.asarray(rows, dtype=np.int64))
+
+
+def sample_keys(item: Item, seed: int, block: int = 128,
+                full_limit: int = 1024) -> np.ndarray:
+    """Key rows (offsets within the item) that a gradient check covers: every
+    key of items up to ``full_limit`` keys; for longer items the first and
+    last key and two seeded random keys of every ``block``-key block (one
+    backward key tile)."""
+    if item.kv_len <= full_limit:
+        return np.arange(item.kv_len, dtype=np.int64)
+    rng = np.random.default_rng([seed, item.kv_off, item.head_begin, 1])
+    keys = []
+    for b0 in range(0, item.kv_len, block):
+        b1 = min(item.kv_len, b0 + block)
+        keys += [b0, b1 - 1]
+        keys += list(rng.integers(b0, b1, size=2))
+    return np.unique(np.asarray(keys, dtype=np.int64))

@@ -26,6 +26,12 @@
  *     exception crosses the ABI. zl_last_error() gives a thread-local text.
  *   - All argument checks run on the host before any HIP call, so a bad
  *     argument never reaches a kernel.
+ *   - Precondition on the data: Q, K, V and dO hold finite values (no NaN,
+ *     no infinity). The kernels are built on that assumption (maxima taken
+ *     without NaN propagation); with non-finite inputs the outputs are
+ *     unspecified, though every launch still runs to completion. The host
+ *     side validates its own float arguments with full IEEE semantics (a
+ *     NaN softmax scale is rejected).
  */
 #ifndef ZL_H_
 #define ZL_H_
@@ -43,7 +49,7 @@ extern "C" {
 enum zl_status {
   ZL_OK = 0,
   ZL_ERR_NULL = -1,     /* a required pointer is NULL */
-  ZL_ERR_SHAPE = -2,    /* head_dim not 64/128, num_heads < 1, negative sizes */
+  ZL_ERR_SHAPE = -2,    /* head_dim not 64/128, num_heads < 1 or too large, negative sizes */
   ZL_ERR_RANGE = -3,    /* an item lies outside the rows or heads */
   ZL_ERR_OVERLAP = -4,  /* two items write the same (query row, head) */
   ZL_ERR_BUFSIZE = -5,  /* host buffer too small */
@@ -58,7 +64,10 @@ enum zl_status {
  * A whole sequence of length L is (q_len = L, kv_len = L, all heads); a
  * theta = (q, h, k) shard holds about L/q queries, H/h heads, L/k keys.
  * q_len = 0 or head_cnt = 0 is a no-op; kv_len = 0 gives O = 0 and
- * LSE = -inf on the item's rows. 32 bytes. */
+ * LSE = -inf on the item's rows. 32 bytes. The six fields are the ones the
+ * work-item table names (q_off, q_len, kv_off, kv_len, head_begin, head_cnt);
+ * they are stored with the two 64-bit offsets first so that the record has
+ * no padding (the Python binding takes them in the table's order). */
 typedef struct zl_item {
   int64_t q_off;
   int64_t kv_off;
@@ -195,11 +204,12 @@ const char* zl_last_error(void);
  * vectors); no device allocation and no HIP call.
  * The caller copies the buffer to device memory unchanged; a worklist is
  * immutable and can serve any number of launches (every layer of a step).
- * Errors: ZL_ERR_NULL, ZL_ERR_SHAPE, ZL_ERR_RANGE, ZL_ERR_OVERLAP,
- * ZL_ERR_BUFSIZE, ZL_ERR_ARG (n_items < 0, n_slots < 0 or > 1<<20,
- * kv_chunk < 0).
- * The schedule is the stable LPT reading of "stably schedules and fuses
- * whole sequences and distributed-attention shards on shared ranks"
+ * Errors: ZL_ERR_NULL, ZL_ERR_SHAPE (head_dim not 64 or 128, num_heads < 1,
+ * num_heads * head_dim > 2^21, negative row counts), ZL_ERR_RANGE,
+ * ZL_ERR_OVERLAP, ZL_ERR_BUFSIZE, ZL_ERR_ARG (n_items < 0, n_slots < 0 or
+ * > 1<<20, kv_chunk < 0, softmax_scale NaN or infinite).
+ * The schedule is a stable LPT list schedule: the reading taken of the
+ * engine's stable scheduling of whole sequences and shards on one rank
  * (pith.science review of arXiv 2608.01150, "What carries the argument"). */
 int zl_build_worklist(const zl_problem* problem, const zl_item* items, int32_t n_items,
                       int32_t n_slots, void* host_buf, size_t* bytes);

@@ -28,7 +28,12 @@ Parity pins (tests/test_oracle.py): brute force without max shift on the
 tiny workload, torch SDPA / logsumexp in float64, closed forms (zero query,
 single key, constant V), invariants (key permutation, key shift, V affine,
 independence across packed sequences), merge == whole attention, finite
-differences and gradient identities for the backward.
+differences and gradient identities for the backward. The sampled forms
+(coalesced_forward_rows, attention_backward_sampled) are pinned at packed
+offsets and head ranges that do not start at zero: the forward rows against
+the pure-Python brute force, the sampled gradients against the full-matrix
+backward (itself pinned by finite differences), each with planted indexing
+mistakes that the pin must catch. No function here is parity unpinned.
 """
 
 from __future__ import annotations
@@ -40,8 +45,8 @@ import numpy as np
 
 __all__ = [
     "attention_rows", "coalesced_forward", "coalesced_forward_rows",
-    "merge_partials", "attention_backward_item", "coalesced_backward",
-    "brute_attention_row",
+    "merge_partials", "attention_backward_item", "attention_backward_sampled",
+    "coalesced_backward", "brute_attention_row",
 ]
 
 
@@ -159,6 +164,53 @@ def attention_backward_item(q, k, v, do, scale: float):
     dq = scale * (ds @ k)
     dk = scale * (ds.T @ q)
     return dq, dk, dv, o, lse
+
+
+def attention_backward_sampled(q, k, v, do, scale: float, rows: Sequence[int],
+                               cols: Sequence[int], chunk: int = 512):
+    """The gradients of attention_backward_item at chosen positions only:
+    dQ at query rows ``rows`` and dK, dV at key rows ``cols`` (offsets within
+    the item), for items too long to hold the whole [q_len, kv_len]
+    probability matrix.
+
+    The definitions are those of attention_backward_item. LSE_r and
+    D_r = sum_c dO_rc O_rc need row r's whole softmax, so every query row is
+    visited, ``chunk`` rows at a time (rows are independent). A sampled key
+    column j needs every query row too: dV_j = sum_r P_rj dO_r and
+    dK_j = scale sum_r dS_rj q_r are sums over all rows, accumulated chunk by
+    chunk. Returns (dq [len(rows), d], dk [len(cols), d], dv [len(cols), d]).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    n_q, d = q.shape
+    dq = np.zeros((rows.size, d))
+    dk = np.zeros((cols.size, d))
+    dv = np.zeros((cols.size, v.shape[1]))
+    if k.shape[0] == 0:
+        return dq, dk, dv
+    for r0 in range(0, n_q, chunk):
+        r1 = min(n_q, r0 + chunk)
+        z = scale * (q[r0:r1] @ k.T)                 # [c, n_k]
+        m = z.max(axis=1, keepdims=True)
+        e = np.exp(z - m)
+        l = e.sum(axis=1, keepdims=True)
+        lse = m[:, 0] + np.log(l[:, 0])
+        o = (e @ v) / l
+        D = (do[r0:r1] * o).sum(axis=1)
+        # key columns: P and dS of this chunk's rows at the sampled keys
+        p_c = np.exp(z[:, cols] - lse[:, None])
+        ds_c = p_c * (do[r0:r1] @ v[cols].T - D[:, None])
+        dv += p_c.T @ do[r0:r1]
+        dk += scale * (ds_c.T @ q[r0:r1])
+        # query rows of this chunk that are sampled: full rows of P and dS
+        sel = np.nonzero((rows >= r0) & (rows < r1))[0]
+        if sel.size:
+            lr = rows[sel] - r0
+            p_r = np.exp(z[lr] - lse[lr, None])
+            ds_r = p_r * (do[rows[sel]] @ v.T - D[lr, None])
+            dq[sel] = scale * (ds_r @ k)
+    return dq, dk, dv
 
 
 def coalesced_backward(Q, K, V, dO, items: Iterable, scale: float):

@@ -18,6 +18,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
 #include <map>
 #include <random>
@@ -187,6 +188,12 @@ static void verify(const zl_problem& p, const std::vector<zl_item>& items, int n
   std::memcpy(bad.data(), b.buf.data(), nb * 8);
   bh->tiles_offset = h->tiles_offset + 8;  // misaligned section
   CHECK(zl::check_worklist(bad.data(), &hv) == ZL_ERR_WORKLIST);
+  std::memcpy(bad.data(), b.buf.data(), nb * 8);
+  bh->softmax_scale = std::nanf("");  // a NaN scale must not pass validation
+  CHECK(zl::check_worklist(bad.data(), &hv) == ZL_ERR_WORKLIST);
+  std::memcpy(bad.data(), b.buf.data(), nb * 8);
+  bh->num_heads = int32_t((zl::kMaxRowElems / bh->head_dim) + 1);  // rows past 2^21 elements
+  CHECK(zl::check_worklist(bad.data(), &hv) == ZL_ERR_WORKLIST);
 }
 
 int main(int argc, char** argv) {
@@ -259,6 +266,12 @@ int main(int argc, char** argv) {
   CHECK(zl_build_worklist(&p, nullptr, 0, -1, nullptr, &bytes) == ZL_ERR_ARG);
   p.kv_chunk = -5;
   CHECK(zl_build_worklist(&p, nullptr, 0, 0, nullptr, &bytes) == ZL_ERR_ARG);
+  p.kv_chunk = 0;
+  p.softmax_scale = std::nanf("");
+  CHECK(zl_build_worklist(&p, nullptr, 0, 0, nullptr, &bytes) == ZL_ERR_ARG);
+  p.softmax_scale = 0.f;
+  p.num_heads = int32_t(zl::kMaxRowElems / 64) + 1;
+  CHECK(zl_build_worklist(&p, nullptr, 0, 0, nullptr, &bytes) == ZL_ERR_SHAPE);
   CHECK(zl::check_worklist(nullptr, nullptr) == ZL_ERR_NULL);
   std::printf("host fuzz: %d worklists verified, %d rejected as expected\n", ok, rejected);
   return 0;

@@ -182,19 +182,25 @@ def test_independence_across_packed_sequences():
     assert not np.allclose(O1[~mask], O2[~mask])
 
 
-def test_isolated_launches_match_the_coalesced_launch_bitwise():
-    """The price table times items alone and per bucket: each (row, head) is
-    computed by the same tile in the same key order either way, so those
-    launches give the coalesced launch's bits."""
+def test_isolated_launches_match_the_oracle_and_the_coalesced_launch():
+    """The price table times items alone and per bucket (the per-(bucket,
+    theta) prices whose sum the pages' planner takes as the step time). Each
+    isolated launch is checked against the oracle on its own (every row of
+    the images, sampled rows of every 128-row block of the shard, on every
+    head); and since each (row, head) is computed by the same tile in the
+    same key order either way, it also gives the coalesced launch's bits."""
     wl = W.config(2)
     items = wl.items[:1] + wl.items[1:3] + wl.items[25:27]
     inp = W.make_inputs(wl)
     q, k, v = to_device(inp)
+    Qh, Kh, Vh = _host(inp.q), _host(inp.k), _host(inp.v)
     _, o, lse = run_fwd(items, q, k, v, wl.num_heads, wl.head_dim)
     O, LSE = o.cpu().numpy(), lse.cpu().numpy()
-    for part in ([items[0]], items[1:3], items[3:]):
+    for part in ([items[0]], items[1:2], items[1:3], items[3:4], items[3:]):
         _, o1, l1 = run_fwd(part, q, k, v, wl.num_heads, wl.head_dim)
         O1, L1 = o1.cpu().numpy(), l1.cpu().numpy()
+        st = oracle_compare(Stats(), part, Qh, Kh, Vh, O1, L1, wl.softmax_scale, seed=41)
+        st.assert_gates(f"isolated launch of {len(part)} item(s), q_len {part[0].q_len}")
         for it in part:
             rs = slice(it.q_off, it.q_off + it.q_len)
             assert np.array_equal(O1[rs], O[rs]) and np.array_equal(L1[rs], LSE[rs])

@@ -1,5 +1,6 @@
 """The host half of libzl (worklist builder and worklist validation) built
-with g++ under AddressSanitizer and UndefinedBehaviorSanitizer, driven by the
+with g++ under AddressSanitizer and UndefinedBehaviorSanitizer, with the same
+compiler and flags as the host object of the shipped library, driven by the
 randomised checks in host_fuzz.cpp. CPU only."""
 
 import os
@@ -11,12 +12,15 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+@pytest.mark.skipif(shutil.which("g++") is None and shutil.which("c++") is None,
+                    reason="no host C++ compiler")
 def test_worklist_builder_under_sanitizers(tmp_path):
     exe = tmp_path / "host_fuzz"
     # The sanitizer runtimes are linked statically so that the executable
     # runs under whatever the environment preloads.
-    cmd = ["g++", "-std=c++17", "-O1", "-g", "-static-libasan", "-static-libubsan", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+    from coalesced_attention_amd.build import HOST_FLAGS, host_cxx
+    cmd = [host_cxx(), *HOST_FLAGS, "-g", "-static-libasan", "-static-libubsan",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-fno-omit-frame-pointer", "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(ROOT, "coalesced_attention_amd", "csrc"),
            os.path.join(ROOT, "coalesced_attention_amd", "csrc", "zl_host.cpp"),

@@ -367,3 +367,164 @@ def _bwd_mutant_dv_transposed_rows(Q, K, V, dO, items, s):
 def test_finite_difference_pin_catches_planted_backward_mistakes(cfg0, mutant):
     wl, inp = cfg0
     assert _fd_check(mutant, wl, inp, n_coords=24, seed=8) > 1e-3
+
+
+# ------------------------------------------------------------ sampled forms
+#
+# The full-size GPU checks go through two sampled forms of the oracle:
+# coalesced_forward_rows (chosen query rows of one item and head) and
+# attention_backward_sampled (dQ at chosen rows, dK / dV at chosen keys).
+# Both are pinned here at packed offsets and head ranges that do not start
+# at zero, where an indexing slip (rows taken from 0 instead of q_off, keys
+# without kv_off, the wrong head) would show.
+
+def _packed_case(seed=31, H=4, d=16):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((300, H, d))
+    K = rng.standard_normal((260, H, d))
+    V = rng.standard_normal((260, H, d))
+    dO = rng.standard_normal((300, H, d))
+    items = [W.Item(37, 90, 21, 150, 1, 2),    # offsets and heads away from 0
+             W.Item(127, 130, 171, 89, 3, 1),  # last head only
+             W.Item(0, 37, 0, 21, 0, 4)]
+    return Q, K, V, dO, items
+
+
+def _rows_check(fn, Q, K, V, items, scale, seed=2):
+    """Largest error of fn (a coalesced_forward_rows-like callable) against
+    the pure-Python brute force at explicit packed indices."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for it in items:
+        rows = np.sort(rng.choice(it.q_len, min(it.q_len, 6), replace=False))
+        for h in range(it.head_begin, it.head_begin + it.head_cnt):
+            o, lse = fn(Q, K, V, it, h, rows, scale)
+            kl = K[it.kv_off:it.kv_off + it.kv_len, h].tolist()
+            vl = V[it.kv_off:it.kv_off + it.kv_len, h].tolist()
+            for i, r in enumerate(rows):
+                bo, blse = orc.brute_attention_row(Q[it.q_off + r, h].tolist(), kl, vl, scale)
+                worst = max(worst, float(np.abs(np.asarray(bo) - o[i]).max()), abs(blse - lse[i]))
+    return worst
+
+
+def test_forward_rows_at_packed_offsets_match_brute_force_and_full_forward(cfg0):
+    Q, K, V, _, items = _packed_case()
+    assert _rows_check(orc.coalesced_forward_rows, Q, K, V, items, 0.25) < 1e-12
+    wl, inp = cfg0
+    Qc, Kc, Vc = (x.astype(np.float64) for x in (inp.q32, inp.k32, inp.v32))
+    assert _rows_check(orc.coalesced_forward_rows, Qc, Kc, Vc, wl.items, wl.softmax_scale) < 1e-12
+    # and the full coalesced forward at the same packed rows
+    O, LSE = orc.coalesced_forward(Q, K, V, items, 0.25)
+    for it in items:
+        rows = np.arange(0, it.q_len, 7)
+        for h in range(it.head_begin, it.head_begin + it.head_cnt):
+            o, lse = orc.coalesced_forward_rows(Q, K, V, it, h, rows, 0.25)
+            np.testing.assert_allclose(o, O[it.q_off + rows, h], atol=1e-13)
+            np.testing.assert_allclose(lse, LSE[it.q_off + rows, h], atol=1e-13)
+
+
+def _rows_mutant_rows_from_zero(Q, K, V, it, h, rows, scale):
+    return orc.attention_rows(Q[rows, h], K[it.kv_off:it.kv_off + it.kv_len, h],
+                              V[it.kv_off:it.kv_off + it.kv_len, h], scale)
+
+
+def _rows_mutant_keys_from_zero(Q, K, V, it, h, rows, scale):
+    return orc.attention_rows(Q[it.q_off + rows, h], K[:it.kv_len, h], V[:it.kv_len, h], scale)
+
+
+def _rows_mutant_head_within_item(Q, K, V, it, h, rows, scale):
+    hh = h - it.head_begin  # head index taken relative to the item
+    return orc.attention_rows(Q[it.q_off + rows, hh], K[it.kv_off:it.kv_off + it.kv_len, hh],
+                              V[it.kv_off:it.kv_off + it.kv_len, hh], scale)
+
+
+@pytest.mark.parametrize("mutant", [_rows_mutant_rows_from_zero, _rows_mutant_keys_from_zero,
+                                    _rows_mutant_head_within_item])
+def test_forward_rows_pin_catches_planted_indexing_mistakes(mutant):
+    Q, K, V, _, items = _packed_case()
+    assert _rows_check(mutant, Q, K, V, items, 0.25) > 1e-3
+
+
+def _sampled_check(fn, Q, K, V, dO, items, scale, chunk, seed=3):
+    """Largest error of fn (an attention_backward_sampled-like callable)
+    against the full-matrix backward at seeded rows and keys of every item
+    and head (all of them for the short items)."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for it in items:
+        rows = np.arange(it.q_len) if it.q_len <= 40 else np.sort(rng.choice(it.q_len, 9, replace=False))
+        cols = np.arange(it.kv_len) if it.kv_len <= 40 else np.sort(rng.choice(it.kv_len, 11, replace=False))
+        for h in range(it.head_begin, it.head_begin + it.head_cnt):
+            args = (Q[it.q_off:it.q_off + it.q_len, h], K[it.kv_off:it.kv_off + it.kv_len, h],
+                    V[it.kv_off:it.kv_off + it.kv_len, h], dO[it.q_off:it.q_off + it.q_len, h])
+            rq, rk, rv, _, _ = orc.attention_backward_item(*args, scale)
+            dq, dk, dv = fn(*args, scale, rows, cols, chunk=chunk)
+            worst = max(worst, float(np.abs(dq - rq[rows]).max(initial=0)),
+                        float(np.abs(dk - rk[cols]).max(initial=0)),
+                        float(np.abs(dv - rv[cols]).max(initial=0)))
+    return worst
+
+
+@pytest.mark.parametrize("chunk", [512, 37, 1])
+def test_backward_sampled_matches_full_matrix_backward(cfg0, chunk):
+    """Row chunks of 37 and 1 cut every item mid-way, so LSE, D and the key
+    sums have to be carried across chunks correctly."""
+    Q, K, V, dO, items = _packed_case()
+    assert _sampled_check(orc.attention_backward_sampled, Q, K, V, dO, items, 0.25, chunk) < 1e-12
+    wl, inp = cfg0
+    Qc, Kc, Vc = (x.astype(np.float64) for x in (inp.q32, inp.k32, inp.v32))
+    dOc = inp.dout.double().numpy()
+    assert _sampled_check(orc.attention_backward_sampled, Qc, Kc, Vc, dOc, wl.items,
+                          wl.softmax_scale, chunk) < 1e-12
+
+
+def test_backward_sampled_all_positions_equal_the_coalesced_backward(cfg0):
+    wl, inp = cfg0
+    Q, K, V = (x.astype(np.float64) for x in (inp.q32, inp.k32, inp.v32))
+    dO = inp.dout.double().numpy()
+    s = wl.softmax_scale
+    it = wl.items[2]
+    dQ, dK, dV = orc.coalesced_backward(Q, K, V, dO, [it], s)
+    for h in range(2):
+        dq, dk, dv = orc.attention_backward_sampled(
+            Q[it.q_off:it.q_off + it.q_len, h], K[it.kv_off:it.kv_off + it.kv_len, h],
+            V[it.kv_off:it.kv_off + it.kv_len, h], dO[it.q_off:it.q_off + it.q_len, h], s,
+            np.arange(it.q_len), np.arange(it.kv_len), chunk=64)
+        np.testing.assert_allclose(dq, dQ[it.q_off:it.q_off + it.q_len, h], atol=1e-12)
+        np.testing.assert_allclose(dk, dK[it.kv_off:it.kv_off + it.kv_len, h], atol=1e-12)
+        np.testing.assert_allclose(dv, dV[it.kv_off:it.kv_off + it.kv_len, h], atol=1e-12)
+        np.testing.assert_allclose(dk.sum(0), 0, atol=1e-11)  # sum_j dS_rj = 0
+
+
+def _sampled_mutant_lse_over_sampled_keys(q, k, v, do, scale, rows, cols, chunk=512):
+    # planted: the softmax normalised over the sampled keys only
+    k, v = np.asarray(k)[cols], np.asarray(v)[cols]
+    return orc.attention_backward_sampled(q, k, v, do, scale, rows, np.arange(len(cols)), chunk=chunk)
+
+
+def _sampled_mutant_key_sums_over_sampled_rows(q, k, v, do, scale, rows, cols, chunk=512):
+    # planted: dK / dV summed over the sampled query rows only
+    dq, _, _ = orc.attention_backward_sampled(q, k, v, do, scale, rows, cols, chunk=chunk)
+    full = orc.attention_backward_item(q, k, v, do, scale)
+    z = scale * (np.asarray(q)[rows] @ np.asarray(k).T)
+    p = np.exp(z - full[4][rows, None])
+    ds = p * (np.asarray(do)[rows] @ np.asarray(v).T - (np.asarray(do)[rows] * full[3][rows]).sum(1)[:, None])
+    return dq, scale * (ds[:, cols].T @ np.asarray(q)[rows]), p[:, cols].T @ np.asarray(do)[rows]
+
+
+def _sampled_mutant_last_chunk_only(q, k, v, do, scale, rows, cols, chunk=512):
+    # planted: key sums reset at every chunk instead of accumulated
+    n = np.asarray(q).shape[0]
+    start = (n - 1) // chunk * chunk
+    dq, _, _ = orc.attention_backward_sampled(q, k, v, do, scale, rows, cols, chunk=chunk)
+    _, dk, dv = orc.attention_backward_sampled(np.asarray(q)[start:], k, v, np.asarray(do)[start:], scale,
+                                               np.zeros(0, np.int64), cols, chunk=chunk)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("mutant", [_sampled_mutant_lse_over_sampled_keys,
+                                    _sampled_mutant_key_sums_over_sampled_rows,
+                                    _sampled_mutant_last_chunk_only])
+def test_backward_sampled_pin_catches_planted_mistakes(mutant):
+    Q, K, V, dO, items = _packed_case()
+    assert _sampled_check(mutant, Q, K, V, dO, items, 0.25, chunk=37) > 1e-3
