@@ -35,7 +35,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "zl.h"
 #include "zl_device.h"
@@ -438,6 +440,81 @@ extern "C" int zl_coalesced_attn_fwd(const void* h_wl, const void* d_wl, const v
   hipStream_t s = static_cast<hipStream_t>(stream);
   const char* dw = static_cast<const char*>(d_wl);
   float* ws = h->ws_rows > 0 ? workspace : nullptr;
+  return h->head_dim == 128 ? launch_fwd<128>(h, dw, q, k, v, o, lse, ws, s)
+                            : launch_fwd<64>(h, dw, q, k, v, o, lse, ws, s);
+}
+
+// ---- allocation-free variant: the key-chunk partials live in a file-scope
+// device array instead of a caller workspace. The array name is a host-side
+// stand-in in host code; its device address is looked up once per device
+// with hipGetSymbolAddress and only that address is handed to kernels.
+namespace {
+
+constexpr int64_t kScratchBytes = ZL_NOALLOC_SCRATCH_BYTES;
+constexpr int64_t kScratchFloats = kScratchBytes / int64_t(sizeof(float));
+constexpr int kMaxDevices = 64;
+
+__device__ __attribute__((aligned(256))) float scratch[kScratchFloats];
+
+std::atomic<float*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (looked up on the first
+// call made with that device current, then cached).
+int scratch_address(int dev, float** out) {
+  float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !addr)
+        return zl::fail(ZL_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+      p = static_cast<float*>(addr);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return ZL_OK;
+}
+
+}  // namespace
+
+extern "C" int zl_coalesced_attn_fwd_noalloc(const void* h_wl, const void* d_wl, const void* q,
+                                             const void* k, const void* v, float* o, float* lse,
+                                             void* stream) {
+  zl::clear_error();
+  const zl_worklist_header* h = nullptr;
+  int rc = zl::check_worklist(h_wl, &h);
+  if (rc) return rc;
+  if (!d_wl || !q || !k || !v || !o || !lse)
+    return zl::fail(ZL_ERR_NULL, "device pointers must be non-NULL");
+  if (!zl::aligned16(d_wl) || !zl::aligned16(q) || !zl::aligned16(k) || !zl::aligned16(v) ||
+      !zl::aligned16(o) || !zl::aligned16(lse))
+    return zl::fail(ZL_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const int64_t need = h->ws_rows * int64_t(h->num_heads) * (h->head_dim + 1);
+  if (need > kScratchFloats)
+    return zl::fail(ZL_ERR_BUFSIZE,
+                    "the worklist's key-chunk partials need %lld bytes; the allocation-free entry "
+                    "point holds %lld (use zl_coalesced_attn_fwd with a caller workspace)",
+                    (long long)(need * int64_t(sizeof(float))), (long long)kScratchBytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* dw = static_cast<const char*>(d_wl);
+  float* ws = nullptr;
+  if (need > 0) {
+    int cur = -1, sdev = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess) return zl::fail(ZL_ERR_HIP, "device query: %s", hipGetErrorString(e));
+    if (sdev != cur)
+      return zl::fail(ZL_ERR_ARG, "stream belongs to device %d but device %d is current", sdev, cur);
+    if (cur < 0 || cur >= kMaxDevices)
+      return zl::fail(ZL_ERR_ARG, "device %d is beyond the %d the library tracks", cur, kMaxDevices);
+    rc = scratch_address(cur, &ws);
+    if (rc) return rc;
+  }
   return h->head_dim == 128 ? launch_fwd<128>(h, dw, q, k, v, o, lse, ws, s)
                             : launch_fwd<64>(h, dw, q, k, v, o, lse, ws, s);
 }

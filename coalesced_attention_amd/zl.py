@@ -25,7 +25,10 @@ WORKLIST_MAGIC = 0x31574C5A
 
 # Symbols include/zl.h declares (checked by the CPU tests).
 EXPORTS = ("zl_abi_version", "zl_status_string", "zl_last_error", "zl_build_worklist",
-           "zl_coalesced_attn_fwd", "zl_merge_partials", "zl_coalesced_attn_bwd")
+           "zl_coalesced_attn_fwd", "zl_merge_partials", "zl_coalesced_attn_bwd",
+           "zl_coalesced_attn_fwd_noalloc")
+# Device scratch the allocation-free forward holds per GPU (ZL_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class ZlError(RuntimeError):
@@ -105,6 +108,8 @@ def _load() -> ctypes.CDLL:
     lib.zl_coalesced_attn_fwd.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, vp]
     lib.zl_merge_partials.restype = ctypes.c_int
     lib.zl_merge_partials.argtypes = [i32, i64, i32, i32, i32, i32, fp, fp, i64, fp, fp, vp]
+    lib.zl_coalesced_attn_fwd_noalloc.restype = ctypes.c_int
+    lib.zl_coalesced_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, fp, fp, vp]
     lib.zl_coalesced_attn_bwd.restype = ctypes.c_int
     lib.zl_coalesced_attn_bwd.argtypes = [vp, vp, vp, vp, vp, fp, fp, vp, fp, fp, fp, fp, vp]
     return lib
@@ -291,6 +296,29 @@ def coalesced_attn_fwd(wl: Worklist, q, k, v, o=None, lse=None, stream=None, wor
     _check(lib.zl_coalesced_attn_fwd(wl.host_ptr(), wl.device.data_ptr(), q.data_ptr(), k.data_ptr(),
                                      v.data_ptr(), o.data_ptr(), lse.data_ptr(), ws_ptr,
                                      _stream_handle(stream, q.device)), "zl_coalesced_attn_fwd")
+    return o, lse
+
+
+def coalesced_attn_fwd_noalloc(wl: Worklist, q, k, v, o, lse, stream=None):
+    """zl_coalesced_attn_fwd_noalloc: the forward into caller-provided ``o``
+    and ``lse`` with the key-chunk partials in the library's own device
+    scratch (no allocation here or in the library). The worklist must
+    already be on the device."""
+    import torch
+    _check_qkv(wl, q, k, v)
+    h = wl.header
+    if wl.device is None:
+        raise ValueError("the worklist must already be on the device (Worklist.to)")
+    if o.dtype != torch.float32 or lse.dtype != torch.float32 or not o.is_contiguous() \
+            or not lse.is_contiguous():
+        raise ValueError("o and lse must be contiguous fp32")
+    if tuple(o.shape) != (h.q_rows, h.num_heads, h.head_dim) or tuple(lse.shape) != (h.q_rows, h.num_heads):
+        raise ValueError("o / lse shape does not match the worklist")
+    _check_device(q.device, o=o, lse=lse)
+    _check(lib.zl_coalesced_attn_fwd_noalloc(wl.host_ptr(), wl.device.data_ptr(), q.data_ptr(),
+                                             k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                             _stream_handle(stream, q.device)),
+           "zl_coalesced_attn_fwd_noalloc")
     return o, lse
 
 

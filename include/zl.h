@@ -269,6 +269,30 @@ int zl_coalesced_attn_bwd(const void* h_wl, const void* d_wl, const void* q, con
                           const void* v, const float* o, const float* lse, const void* dout,
                           float* dq, float* dk, float* dv, float* d_ws, void* stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same computation, arguments and errors as
+ * zl_coalesced_attn_fwd, except that the key-chunk partials of a worklist
+ * built with kv_chunk > 0 go to a scratch array that the library holds in
+ * device memory (ZL_NOALLOC_SCRATCH_BYTES on each GPU it runs on, kept until
+ * the process ends) instead of a caller workspace. It calls no hipMalloc,
+ * hipFree or allocating routine.
+ * - A worklist whose partials need more than ZL_NOALLOC_SCRATCH_BYTES
+ *   (ws_rows * num_heads * (head_dim + 1) * 4 bytes) is rejected with
+ *   ZL_ERR_BUFSIZE before any HIP call.
+ * - The scratch of a GPU is looked up on the first call that needs it, with
+ *   that GPU current; `stream` must belong to the current device
+ *   (ZL_ERR_ARG otherwise).
+ * - Every call on one GPU shares that GPU's scratch and it keeps the last
+ *   call's contents: calls that overlap in time on one GPU (different
+ *   streams, or host threads) race and give undefined results; calls in
+ *   order on one stream are safe. Nothing needs clearing: each partial is
+ *   written in full before the merge reads it. */
+#define ZL_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int zl_coalesced_attn_fwd_noalloc(const void* h_wl, const void* d_wl, const void* q,
+                                  const void* k, const void* v, float* o, float* lse,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -219,3 +219,25 @@ def test_nan_and_oversized_shapes_are_rejected_by_the_shipped_library():
         assert fwd(bad.ctypes.data, p, p, p, p, p, p, None, None) == -7, field
         assert bwd(bad.ctypes.data, p, p, p, p, p, p, p, p, p, p, p, None) == -7, field
         assert b"header" in zl.lib.zl_last_error()
+
+
+def test_noalloc_forward_rejects_bad_arguments_before_any_hip_call():
+    """The allocation-free forward checks the worklist, pointers and the size
+    of its key-chunk partials against the library's scratch on the host."""
+    p = 1 << 20  # aligned fake device address; never dereferenced on these paths
+    f = zl.lib.zl_coalesced_attn_fwd_noalloc
+    wl = W.config(0)
+    built = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim)
+    assert f(None, p, p, p, p, p, p, None) == -1
+    assert f(built.host_ptr(), None, p, p, p, p, p, None) == -1
+    assert f(built.host_ptr(), p, p + 8, p, p, p, p, None) == -6
+    bad = built.host.copy()
+    zl.WorklistHeader.from_buffer(bad).softmax_scale = float("nan")
+    assert f(bad.ctypes.data, p, p, p, p, p, p, None) == -7
+    big = zl.build_worklist([(0, 6000, 0, 8000, 0, 24)], 6000, 8000, 24, 128, kv_chunk=2000)
+    assert 4 * big.workspace_floats > zl.NOALLOC_SCRATCH_BYTES
+    assert f(big.host_ptr(), p, p, p, p, p, p, None) == -5
+    assert b"allocation-free" in zl.lib.zl_last_error()
+    text = open(HEADER).read()
+    assert zl.NOALLOC_SCRATCH_BYTES == eval(re.search(r"#define ZL_NOALLOC_SCRATCH_BYTES \((\d+)ll << (\d+)\)",
+                                                      text).expand(r"\1 << \2"))
