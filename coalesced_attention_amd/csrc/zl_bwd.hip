@@ -230,7 +230,7 @@ __device__ __forceinline__ void dq_tile(const zl_tile& tile, const __bf16* __res
       issue_tile(kbase, kstage(b), b);
       issue_tile(vbase, vstage(b), b);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitLoads + 4 * kLoadsPerTile);  // K(-1), K(0), V(0) landed
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * kLoadsPerTile));  // K(-1), K(0), V(0) landed
     lds_barrier();
     f32x16 s_a = f32x16{}, d_a = f32x16{}, s_b, d_b;
     bf16x8 x_a[2], x_b[2] = {bf16x8{}, bf16x8{}};
@@ -308,7 +308,7 @@ __device__ __forceinline__ void dq_tile(const zl_tile& tile, const __bf16* __res
     for (int J = 0; J < nblk; ++J) {
       half_step(J, 0, s_a, d_a, s_b, d_b, x_a, x_b);
       // K(J+1), V(J+1) landed: only the two loads of the previous barrier may fly
-      __builtin_amdgcn_s_waitcnt(kWaitLoads + 2 * kLoadsPerTile);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerTile));
       lds_barrier();
       issue_tile(kbase, kstage(J + C::kAhead), J + C::kAhead);
       issue_tile(vbase, vstage(J + C::kAhead), J + C::kAhead);
@@ -429,11 +429,11 @@ __device__ __forceinline__ void dkdv_tile(const zl_tile& tile, const __bf16* __r
   // issued in this iteration (if any) may still fly
   auto wait_older = [&](bool issued) __attribute__((always_inline)) {
     if (!issued)
-      __builtin_amdgcn_s_waitcnt(kWaitLoads);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     else if (wave >= C::kWaves - 2)
-      __builtin_amdgcn_s_waitcnt(kWaitLoads + C::kLoadsPerWave + 1);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::kLoadsPerWave + 1));
     else
-      __builtin_amdgcn_s_waitcnt(kWaitLoads + C::kLoadsPerWave);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::kLoadsPerWave));
   };
 
   // exchange buffer: operand `kind` (0 = P, 1 = dS), half `u` of pair `pair`

@@ -24,9 +24,14 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kXcds = 8;               // accelerator complex dies of an MI355X
-// s_waitcnt immediate with lgkmcnt and expcnt at their maximum and vmcnt 0:
-// adding n waits until at most n vector-memory operations are outstanding.
-constexpr int kWaitLoads = 0x0F70;
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (lgkmcnt and expcnt left at their maximum).
+// vmcnt is six bits on gfx9-family parts, split over bits [3:0] and [15:14].
+__host__ __device__ constexpr int wait_vmcnt(int n) {
+  return (n & 0xF) | ((n >> 4) << 14) | 0x0F70;
+}
+static_assert(wait_vmcnt(0) == 0x0F70 && wait_vmcnt(17) == 0x4F71 && wait_vmcnt(63) == 0xCF7F,
+              "vmcnt encoding");
 // Buffer resource word 3 for raw (untyped) dword loads on gfx9-family parts.
 constexpr int kBufferFlags = 0x00020000;
 

@@ -222,7 +222,7 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
     issue_tile(kbase, kstage(1), 1);
     issue_tile(vbase, vstage(0), 0);
     issue_tile(kbase, kstage(2), 2);
-    __builtin_amdgcn_s_waitcnt(kWaitLoads + 4 * kLoadsPerTile);  // K(0) landed
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * kLoadsPerTile));  // K(0) landed
     lds_barrier();
     f32x16 s_a[KB], s_b[KB];
     bf16x8 p_a[KB][2], p_b[KB][2];

@@ -37,9 +37,10 @@ constexpr int kCostC0PerRow = 64;
 // Largest static slot count accepted by zl_build_worklist.
 constexpr int kMaxSlots = 1 << 20;
 // Largest num_heads * head_dim (elements of one packed row). The kernels form
-// byte offsets of up to 256 rows of bf16 inside a buffer resource in 32-bit
-// arithmetic: 256 * 2^21 * 2 bytes = 2^30 stays clear of overflow.
-constexpr int64_t kMaxRowElems = int64_t(1) << 21;
+// byte offsets of up to 256 rows inside a buffer resource in 32-bit
+// arithmetic: 256 rows * 2^20 elements * 4 bytes (fp32 O) = 2^30 stays clear
+// of overflow.
+constexpr int64_t kMaxRowElems = int64_t(1) << 20;
 
 // Merge the key-chunk partials of every split item of a worklist (its merge
 // list) from the forward workspace into O / LSE, one launch on `stream`.

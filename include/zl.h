@@ -205,7 +205,7 @@ const char* zl_last_error(void);
  * The caller copies the buffer to device memory unchanged; a worklist is
  * immutable and can serve any number of launches (every layer of a step).
  * Errors: ZL_ERR_NULL, ZL_ERR_SHAPE (head_dim not 64 or 128, num_heads < 1,
- * num_heads * head_dim > 2^21, negative row counts), ZL_ERR_RANGE,
+ * num_heads * head_dim > 2^20, negative row counts), ZL_ERR_RANGE,
  * ZL_ERR_OVERLAP, ZL_ERR_BUFSIZE, ZL_ERR_ARG (n_items < 0, n_slots < 0 or
  * > 1<<20, kv_chunk < 0, softmax_scale NaN or infinite).
  * The schedule is a stable LPT list schedule: the reading taken of the

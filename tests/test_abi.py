@@ -200,20 +200,20 @@ def test_nan_and_oversized_shapes_are_rejected_by_the_shipped_library():
     built without the kernels' finite-math flag): a NaN softmax scale is
     rejected when the worklist is built and when a tampered header reaches
     the forward or backward entry point, before any HIP call. Rows of more
-    than 2^21 elements (num_heads * head_dim) are rejected too, so the
+    than 2^20 elements (num_heads * head_dim) are rejected too, so the
     kernels' 32-bit in-buffer offsets cannot wrap."""
     ok = [(0, 10, 0, 10, 0, 4)]
     assert _rc_build(ok, scale=float("nan")) == -9
     assert _rc_build(ok, scale=float("-nan")) == -9
-    assert _rc_build(ok, H=(1 << 21) // 128) == 0
-    assert _rc_build([(0, 10, 0, 10, 0, 4)], H=(1 << 21) // 128 + 1) == -2
-    assert _rc_build([(0, 10, 0, 10, 0, 4)], H=(1 << 21) // 64 + 1, d=64) == -2
+    assert _rc_build(ok, H=(1 << 20) // 128) == 0
+    assert _rc_build([(0, 10, 0, 10, 0, 4)], H=(1 << 20) // 128 + 1) == -2
+    assert _rc_build([(0, 10, 0, 10, 0, 4)], H=(1 << 20) // 64 + 1, d=64) == -2
     wl = W.config(0)
     built = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim)
     p = 1 << 20  # aligned fake device address; never dereferenced on these paths
     fwd, bwd = zl.lib.zl_coalesced_attn_fwd, zl.lib.zl_coalesced_attn_bwd
     for field, value in (("softmax_scale", float("nan")), ("softmax_scale", -1.0),
-                         ("softmax_scale", 0.0), ("num_heads", (1 << 21) // 64 + 1)):
+                         ("softmax_scale", 0.0), ("num_heads", (1 << 20) // 64 + 1)):
         bad = built.host.copy()
         setattr(zl.WorklistHeader.from_buffer(bad), field, value)
         assert fwd(bad.ctypes.data, p, p, p, p, p, p, None, None) == -7, field
