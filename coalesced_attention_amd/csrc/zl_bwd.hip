@@ -25,20 +25,21 @@
 // beside the S / dP MFMAs of the next and the dQ MFMAs of the previous.
 // It also computes D for its rows and stores it for dkdv_kernel.
 //
-// dkdv_kernel: one tile = 128 keys of one item on one head, against all of
+// dkdv_kernel: one tile = 256 keys of one item on one head, against all of
 // the item's queries, streamed through LDS 32 rows at a time (Q, dO, LSE, D;
-// direct-to-LDS loads, a 4-step ring, two steps ahead). 8 waves in 4
-// producer / consumer pairs, one of each per SIMD, 32 keys per pair:
-//   producer: K, V rows of its keys in registers (B operands);
-//             S = Q K^T, dP = dO V^T (A = Q / dO rows; lane = key),
-//             P = exp2(S c - LSE2), dS = s P (dP - D), packed to bf16 and
-//             written to an LDS exchange buffer exactly as held in registers
-//   consumer: one step behind, dV^T += dO^T P, dK^T += Q^T dS (A = dO^T /
-//             Q^T transpose reads, B = the producer's registers from LDS);
-//             holds the dK^T / dV^T accumulators
-// so the exponentials of one wave run beside the MFMAs of the other. One
-// barrier per step. At the end dK^T / dV^T go through LDS to coalesced fp32
-// atomics (items may share key/value rows, whose gradients add up).
+// direct-to-LDS loads, a 4-step ring, two steps ahead). Each of the 8 waves
+// (two per SIMD) owns 32 keys and runs all four products for them:
+//   S = Q K^T, dP = dO V^T          (A = Q / dO rows from LDS; B = the wave's
+//                                    K rows held in registers, V rows read
+//                                    from the tile's V staged once in LDS;
+//                                    lane = key)
+//   P = exp2(S c - LSE log2 e), dS = P (s dP - s D), packed to bf16 in place
+//   dV^T += dO^T P, dK^T += Q^T dS  (A = dO^T / Q^T transpose reads whose
+//                                    query order matches the accumulator's)
+// so no operand leaves the wave, and the exponentials of one wave run beside
+// the MFMAs of the other wave on its SIMD. One barrier per step. At the end
+// dK^T / dV^T go through LDS to coalesced fp32 atomics (items may share
+// key/value rows, whose gradients add up).
 
 #include <hip/hip_runtime.h>
 
@@ -54,10 +55,9 @@ using namespace zl::dev;
 
 template <int D>
 struct Bwd {
-  static constexpr int kPairs = zl::kBwdPairs;
-  static constexpr int kWaves = 2 * kPairs;
+  static constexpr int kWaves = zl::kBwdWaves;
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kBN = zl::kBwdBlockN;  // keys per tile, 32 per pair
+  static constexpr int kBN = zl::kBwdBlockN;  // keys per tile, 32 per wave
   static constexpr int kBM = zl::kBwdBlockM;  // query rows per step
   static constexpr int kDS = D / 16;
   static constexpr int kDB = D / 32;
@@ -72,18 +72,18 @@ struct Bwd {
   static constexpr int kOffDO = kRing * kQTile;       // kRing stages
   static constexpr int kLSlot = 512;                  // LSE[64] then D[64], fp32
   static constexpr int kOffL = 2 * kRing * kQTile;    // kRing slots
-  static constexpr int kXPair = 4 * 64 * 16;          // P[2], dS[2] operands of one pair
-  static constexpr int kXBuf = kPairs * kXPair;
-  static constexpr int kOffX = kOffL + kRing * kLSlot;  // 2 buffers
-  static constexpr int kLdsBytes = kOffX + 2 * kXBuf;
+  static constexpr int kVGroups = kBN / kG;           // the tile's V rows
+  static constexpr int kOffV = kOffL + kRing * kLSlot;
+  static constexpr int kLdsBytes = kOffV + kVGroups * kGB;
   // per wave and step: Q and dO groups spread over all waves, and one more
-  // load (LSE or D) on the last two waves
+  // load (LSE or D) on the last two waves; per wave and tile: its share of V
   static constexpr int kLoadsPerWave = 2 * kQGroups / kWaves;
-  // dK^T / dV^T flush: [kBN][D] fp32 with a 16-byte row pad, over the Q/dO ring
+  static constexpr int kVLoadsPerWave = kVGroups / kWaves;
+  // dK^T / dV^T flush: [kBN][D] fp32 with a 16-byte row pad, over the whole LDS
   static constexpr int kFlushPitch = D * 4 + 16;
-  static_assert(kBN == kPairs * 32 && kBM == 32, "shapes");
-  static_assert((2 * kQGroups) % kWaves == 0, "loads spread evenly");
-  static_assert(kBN * kFlushPitch <= kOffL, "flush buffer fits the Q/dO ring");
+  static_assert(kBN == kWaves * 32 && kBM == 32, "shapes");
+  static_assert((2 * kQGroups) % kWaves == 0 && kVGroups % kWaves == 0, "loads spread evenly");
+  static_assert(kBN * kFlushPitch <= kLdsBytes, "flush buffer fits the LDS");
 };
 
 // dq_kernel: the forward's tile shape and LDS layout, 64-key blocks.
@@ -383,12 +383,11 @@ __device__ __forceinline__ void dkdv_tile(const zl_tile& tile, const __bf16* __r
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool producer = wave < C::kPairs;  // waves w and w + 4 share SIMD w % 4
-  const int pair = producer ? wave : wave - C::kPairs;
   const int l32 = lane & 31;
   const int half = lane >> 5;
   const int64_t rs = int64_t(H) * D;
   const int nsteps = (tile.q_rows + C::kBM - 1) / C::kBM;
+  const float c = scale * kLog2e;
 
   // ---- direct-to-LDS loads of step `step`: Q and dO rows (rows at or past
   // the item's end read as zero), and on waves 6 / 7 the LSE / D values
@@ -436,151 +435,140 @@ __device__ __forceinline__ void dkdv_tile(const zl_tile& tile, const __bf16* __r
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::kLoadsPerWave));
   };
 
-  // exchange buffer: operand `kind` (0 = P, 1 = dS), half `u` of pair `pair`
-  auto xoff = [&](int step, int kind, int u) __attribute__((always_inline)) {
-    return C::kOffX + (step & 1) * C::kXBuf + pair * C::kXPair + (kind * 2 + u) * 1024 + lane * 16;
-  };
-
-  // prologue: steps 0 and 1
+  // ---- this lane's key: K row in registers (B of S = Q K^T: k = head_dim,
+  // j = key), V rows of the whole tile in LDS (B of dP = dO V^T)
+  const int key = wave * 32 + l32;
+  const bool kvalid = key < tile.kv_len;
+  bf16x8 kf[DS];
+  {
+    const int64_t kr = tile.kv_row0 + (kvalid ? key : 0);
+    const int64_t off = kr * rs + int64_t(tile.head) * D + 8 * half;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(K + off + ds * 16);
+      kf[ds] = kvalid ? a : bf16x8{};
+    }
+  }
+  {
+    const __bf16* base = V + tile.kv_row0 * rs + int64_t(tile.head) * D;
+    const int64_t addr = uniform_i64(reinterpret_cast<int64_t>(base));
+    const int rows = __builtin_amdgcn_readfirstlane(min(C::kBN, tile.kv_len));
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<__bf16*>(addr), 0,
+                                                        rows * int(rs) * 2, kBufferFlags);
+#pragma unroll
+    for (int i = 0; i < C::kVLoadsPerWave; ++i) {
+      const int g = wave * C::kVLoadsPerWave + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void ZL_LDS*)(smem + C::kOffV + g * GB), 16,
+                                               ld_lane,
+                                               __builtin_amdgcn_readfirstlane(g * G * int(rs) * 2),
+                                               0, 0);
+    }
+  }
+  // prologue: V, steps 0 and 1
   issue_step(0);
   if (nsteps > 1) issue_step(1);
   wait_older(nsteps > 1);
-  __syncthreads();
+  lds_barrier();
 
-  const int key = pair * 32 + l32;
-  const bool kvalid = key < tile.kv_len;
-  // flush of one of dK / dV staged in LDS as [key][d] fp32 by the consumers:
-  // every thread adds a strided share with coalesced fp32 atomics
-  auto add_staged = [&](float* __restrict__ out) __attribute__((always_inline)) {
+  // row reads (A of S and dP, B of dP): row l32, chunk 2*ds + half
+  const int a_lane = (l32 / G) * GB + (half * G + l32 % G) * 16;
+  const int v_lane = C::kOffV + (wave * 32 / G) * GB + a_lane;
+  // transpose reads of Q^T / dO^T (A of dK^T / dV^T): rows in the order the
+  // S accumulator keeps them, 4*half + e and 8 + 4*half + e
+  const int e_l = (lane & 15) >> 2;
+  const int c_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tq_lane = ((4 * half + e_l) / G) * GB + (c_l * G + (4 * half + e_l) % G) * 16 + (lane & 1) * 8;
+  constexpr int kPlus8 = (8 / G) * GB + (8 % G) * 16;  // 8 rows further
+  auto tr8 = [&](int a) __attribute__((always_inline)) {
+    const i16x4 lo = lds_read_tr16(smem + a);
+    const i16x4 hi = lds_read_tr16(smem + a + kPlus8);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+  for (int j = 0; j < nsteps; ++j) {
+    const bool issue = j + 2 < nsteps;
+    if (issue) issue_step(j + 2);
+    const int slot = j % C::kRing;
+    int qa = C::kOffQ + slot * C::kQTile + a_lane;
+    int ga = C::kOffDO + slot * C::kQTile + a_lane;
+    int va = v_lane;
+    asm volatile("" : "+v"(qa), "+v"(ga), "+v"(va));
+    // S = Q K^T, dP = dO V^T (lane = key; register r holds query 8*(r/4) + 4*half + r%4)
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(smem + qa + ds * 2 * G * 16), kf[ds], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(smem + ga + ds * 2 * G * 16),
+                                                   lds_read_b128(smem + va + ds * 2 * G * 16), dp, 0, 0, 0);
+    }
+    // P = exp2(S c - LSE log2 e), dS = P (s dP - s D), packed as the B operands
+    // of dV^T += dO^T P and dK^T += Q^T dS. Keys at or past kv_len have zero
+    // K / V rows; their P and dS only reach dV / dK columns of those keys,
+    // which are not stored.
+    const char ZL_LDS* ls = smem + C::kOffL + slot * C::kLSlot;
+    u32x4 pk[2], sk[2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 lse = *reinterpret_cast<const f32x4 ZL_LDS*>(ls + (8 * g + 4 * half) * 4);
+      const f32x4 dd = *reinterpret_cast<const f32x4 ZL_LDS*>(ls + 256 + (8 * g + 4 * half) * 4);
+      float p[4], d[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + e], c, -lse[e] * kLog2e));
+        d[e] = fmaf(dp[4 * g + e], scale, -dd[e]) * p[e];
+      }
+      pk[g >> 1][2 * (g & 1)] = pack_bf16x2(p[0], p[1]);
+      pk[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p[2], p[3]);
+      sk[g >> 1][2 * (g & 1)] = pack_bf16x2(d[0], d[1]);
+      sk[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(d[2], d[3]);
+    }
+    int qt = C::kOffQ + slot * C::kQTile + tq_lane;
+    int gt = C::kOffDO + slot * C::kQTile + tq_lane;
+    asm volatile("" : "+v"(qt), "+v"(gt));
+    // k-slot e of operand u in half h is query 16u + 8(e/4) + 4h + e%4
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pk[u]);
+      const bf16x8 sf = __builtin_bit_cast(bf16x8, sk[u]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int off = ((16 * u) / G) * GB + db * 4 * G * 16;
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr8(gt + off), pf, dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr8(qt + off), sf, dk[db], 0, 0, 0);
+      }
+    }
+    wait_older(issue);
+    lds_barrier();
+  }
+
+  // ---- dK^T then dV^T -> LDS [key][d] fp32 (over the whole LDS, no longer
+  // read; register r of block db is d = db*32 + 8(r/4) + 4*half + r%4), then
+  // every thread adds a strided share with coalesced fp32 atomics (items may
+  // share key/value rows, whose gradients add up)
+#pragma unroll
+  for (int kind = 0; kind < 2; ++kind) {
+    const f32x16 (&acc)[DB] = kind == 0 ? dk : dv;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = {acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+        *reinterpret_cast<f32x4 ZL_LDS*>(smem + key * C::kFlushPitch + (db * 32 + 8 * g + 4 * half) * 4) = x;
+      }
+    __syncthreads();
+    float* __restrict__ out = kind == 0 ? dK : dV;
     for (int idx = tid; idx < tile.kv_len * D; idx += C::kThreads) {
       const int kr = idx / D, col = idx % D;
       const float x = *reinterpret_cast<const float ZL_LDS*>(smem + kr * C::kFlushPitch + col * 4);
       atomicAdd(out + ((tile.kv_row0 + kr) * H + tile.head) * D + col, x);
     }
-  };
-  if (producer) {
-    // ---- K / V rows of this lane's key (k = head_dim, j = key)
-    bf16x8 kf[DS], vf[DS];
-    {
-      const int64_t kr = tile.kv_row0 + (kvalid ? key : 0);
-      const int64_t off = kr * rs + int64_t(tile.head) * D + 8 * half;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(K + off + ds * 16);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(V + off + ds * 16);
-        kf[ds] = kvalid ? a : bf16x8{};
-        vf[ds] = kvalid ? b : bf16x8{};
-      }
-    }
-    const float c = scale * kLog2e;
-    // row reads (A of S and dP): row l32, chunk 2*ds + half
-    const int a_lane = (l32 / G) * GB + (half * G + l32 % G) * 16;
-    for (int j = 0; j <= nsteps; ++j) {
-      const bool issue = j + 2 < nsteps;
-      if (issue) issue_step(j + 2);
-      if (j < nsteps) {
-        const int slot = j % C::kRing;
-        int qa = C::kOffQ + slot * C::kQTile + a_lane;
-        int ga = C::kOffDO + slot * C::kQTile + a_lane;
-        asm volatile("" : "+v"(qa), "+v"(ga));
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(smem + qa + ds * 2 * G * 16), kf[ds], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(smem + ga + ds * 2 * G * 16), vf[ds], dp, 0, 0, 0);
-        }
-        // register r holds query 8*(r/4) + 4*half + r%4
-        const char ZL_LDS* ls = smem + C::kOffL + slot * C::kLSlot;
-        bf16x8 pf[2], sf[2];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 lse = *reinterpret_cast<const f32x4 ZL_LDS*>(ls + (8 * g + 4 * half) * 4);
-          const f32x4 dd = *reinterpret_cast<const f32x4 ZL_LDS*>(ls + 256 + (8 * g + 4 * half) * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            // keys at or past kv_len have zero K / V rows; their P and dS
-            // only reach dV / dK columns of those keys, which are not stored
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse[e] * kLog2e));
-            pf[r >> 3][r & 7] = (__bf16)p;
-            sf[r >> 3][r & 7] = (__bf16)(fmaf(dp[r], scale, -dd[e]) * p);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          *reinterpret_cast<bf16x8 ZL_LDS*>(smem + xoff(j, 0, u)) = pf[u];
-          *reinterpret_cast<bf16x8 ZL_LDS*>(smem + xoff(j, 1, u)) = sf[u];
-        }
-      }
-      wait_older(issue);
-      lds_barrier();
-    }
-    // the consumers stage dK, then dV
-#pragma unroll
-    for (int kind = 0; kind < 2; ++kind) {
-      __syncthreads();
-      add_staged(kind == 0 ? dK : dV);
-      __syncthreads();
-    }
-  } else {
-    f32x16 dk[DB], dv[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i) {
-      dk[i] = f32x16{};
-      dv[i] = f32x16{};
-    }
-    // transpose reads of Q^T / dO^T (A of dK^T / dV^T): rows in the order the
-    // producer's S accumulator keeps them, 4*half + e and 8 + 4*half + e
-    const int e_l = (lane & 15) >> 2;
-    const int c_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    const int tq_lane = ((4 * half + e_l) / G) * GB + (c_l * G + (4 * half + e_l) % G) * 16 + (lane & 1) * 8;
-    constexpr int kPlus8 = (8 / G) * GB + (8 % G) * 16;  // 8 rows further
-    auto tr8 = [&](int a) __attribute__((always_inline)) {
-      const i16x4 lo = lds_read_tr16(smem + a);
-      const i16x4 hi = lds_read_tr16(smem + a + kPlus8);
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    for (int j = 0; j <= nsteps; ++j) {
-      const bool issue = j + 2 < nsteps;
-      if (issue) issue_step(j + 2);
-      if (j > 0) {
-        const int st = j - 1;  // the producer wrote this step last iteration
-        const int slot = st % C::kRing;
-        int qa = C::kOffQ + slot * C::kQTile + tq_lane;
-        int ga = C::kOffDO + slot * C::kQTile + tq_lane;
-        asm volatile("" : "+v"(qa), "+v"(ga));
-        // k-slot e of operand u in half h is query 16u + 8(e/4) + 4h + e%4
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8 pf = *reinterpret_cast<const bf16x8 ZL_LDS*>(smem + xoff(st, 0, u));
-          const bf16x8 sf = *reinterpret_cast<const bf16x8 ZL_LDS*>(smem + xoff(st, 1, u));
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int off = ((16 * u) / G) * GB + db * 4 * G * 16;
-            dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr8(ga + off), pf, dv[db], 0, 0, 0);
-            dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr8(qa + off), sf, dk[db], 0, 0, 0);
-          }
-        }
-      }
-      wait_older(issue);
-      lds_barrier();
-    }
-    // ---- dK^T then dV^T -> LDS [key][d] fp32 (over the Q/dO ring, no longer
-    // read; register r of block db is d = db*32 + 8(r/4) + 4*half + r%4)
-#pragma unroll
-    for (int kind = 0; kind < 2; ++kind) {
-      const f32x16 (&acc)[DB] = kind == 0 ? dk : dv;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 x = {acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
-          *reinterpret_cast<f32x4 ZL_LDS*>(smem + key * C::kFlushPitch + (db * 32 + 8 * g + 4 * half) * 4) = x;
-        }
-      __syncthreads();
-      add_staged(kind == 0 ? dK : dV);
-      __syncthreads();
-    }
+    __syncthreads();
   }
 }
 

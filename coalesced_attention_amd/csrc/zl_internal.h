@@ -25,10 +25,9 @@ static_assert(kFwdBlockM == 256, "the worklist cuts 256-row tiles");
 static_assert(sizeof(zl_worklist_header) == 192 && sizeof(zl_tile) == 32 &&
                   sizeof(zl_outmap) == 16 && sizeof(zl_merge) == 32,
               "ABI record sizes");
-// dK/dV backward tile: 4 producer / consumer wave pairs x 32 keys, streaming
-// 32 query rows per step.
-constexpr int kBwdPairs = 4;
-constexpr int kBwdBlockN = kBwdPairs * 32;
+// dK/dV backward tile: 8 waves x 32 keys, streaming 32 query rows per step.
+constexpr int kBwdWaves = 8;
+constexpr int kBwdBlockN = kBwdWaves * 32;
 constexpr int kBwdBlockM = 32;
 
 // Per-tile fixed cost in (query row x key) units used by the LPT rule: the
