@@ -37,7 +37,7 @@
 //   dV^T += dO^T P, dK^T += Q^T dS  (A = dO^T / Q^T transpose reads whose
 //                                    query order matches the accumulator's)
 // so no operand leaves the wave, and the exponentials of one wave run beside
-// the MFMAs of the other wave on its SIMD. One barrier per step. At the end
+// the MFMAs of the other wave on its SIMD. One barrier per two steps. At the end
 // dK^T / dV^T go through LDS to coalesced fp32 atomics (items may share
 // key/value rows, whose gradients add up).
 
@@ -424,17 +424,6 @@ __device__ __forceinline__ void dkdv_tile(const zl_tile& tile, const __bf16* __r
                                                0, 0, 0);
     }
   };
-  // wait until this wave's loads of earlier steps have landed; the loads
-  // issued in this iteration (if any) may still fly
-  auto wait_older = [&](bool issued) __attribute__((always_inline)) {
-    if (!issued)
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-    else if (wave >= C::kWaves - 2)
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::kLoadsPerWave + 1));
-    else
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::kLoadsPerWave));
-  };
-
   // ---- this lane's key: K row in registers (B of S = Q K^T: k = head_dim,
   // j = key), V rows of the whole tile in LDS (B of dP = dO V^T)
   const int key = wave * 32 + l32;
@@ -464,10 +453,14 @@ __device__ __forceinline__ void dkdv_tile(const zl_tile& tile, const __bf16* __r
                                                0, 0);
     }
   }
-  // prologue: V, steps 0 and 1
+  // prologue: V, steps 0 and 1. The workgroup meets after every odd step:
+  // that barrier waits for every load issued so far, i.e. the rows of the
+  // next two steps. Step x's loads go out at the top of step x - 2 into the
+  // ring slot of step x - 4, whose last readers finished before the barrier
+  // that follows step x - 4 or x - 3, whichever is odd.
   issue_step(0);
   if (nsteps > 1) issue_step(1);
-  wait_older(nsteps > 1);
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
   lds_barrier();
 
   // row reads (A of S and dP, B of dP): row l32, chunk 2*ds + half
@@ -543,9 +536,12 @@ __device__ __forceinline__ void dkdv_tile(const zl_tile& tile, const __bf16* __r
         dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr8(qt + off), sf, dk[db], 0, 0, 0);
       }
     }
-    wait_older(issue);
-    lds_barrier();
+    if (j & 1) {
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+      lds_barrier();
+    }
   }
+  lds_barrier();  // every wave is done with the ring and V
 
   // ---- dK^T then dV^T -> LDS [key][d] fp32 (over the whole LDS, no longer
   // read; register r of block db is d = db*32 + 8(r/4) + 4*half + r%4), then
