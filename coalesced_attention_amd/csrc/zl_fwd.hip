@@ -15,7 +15,8 @@
 //   - wave w owns query rows [32w, 32w+32) of the tile; lane l owns query
 //     row l%32 and half h = l/32 of that row's keys in every 32-key block.
 //   - scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held in registers).
+//     v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held in registers;
+//     the tile's Q rows arrive through LDS with the same direct loads as K/V).
 //     In the accumulator layout a lane then holds 16 keys of ONE query, so
 //     the row max is an in-lane reduction plus one v_permlane32_swap, and
 //     the running sum needs no exchange until the epilogue.
@@ -104,18 +105,11 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
   const int half = lane >> 5;
   const int64_t rs = int64_t(H) * D;  // elements between consecutive rows
 
-  // ---- Q^T fragments: query row wave*32 + l32, head_dim [ds*16 + 8*half, +8)
+  // ---- Q^T fragments (read in the prologue): query row wave*32 + l32,
+  // head_dim [ds*16 + 8*half, +8)
   const int qr = wave * 32 + l32;
   const bool qvalid = qr < tile.q_rows;
   bf16x8 qf[DS];
-  {
-    const __bf16* qp = Q + (tile.q_row0 + (qvalid ? qr : 0)) * rs + int64_t(tile.head) * D + 8 * half;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + ds * 16);
-      qf[ds] = qvalid ? x : bf16x8{};
-    }
-  }
 
   const int kv_len = tile.kv_len;
   const int nblk = (kv_len + C::kBN - 1) / C::kBN;
@@ -213,17 +207,46 @@ __device__ __forceinline__ void run_tile(const zl_tile& tile, const __bf16* __re
   float l_part = 0.f;       // this lane's partial row sum, relative to m_use
 
   if (nblk > 0) {
-    // ---- prologue: K(0..2), a zero V stage for the empty PV of iteration 0,
-    // V(0); S(0) and its max. Only K(0) is waited for before S(0); the other
-    // loads land while its MFMAs run.
+    // ---- prologue: K(0), the Q rows, K(1), V(0), K(2); S(0) and its max.
+    // Only K(0) and Q are waited for before S(0); the other loads land while
+    // its MFMAs run.
     static_assert(C::kKAhead == 3 && C::kVAhead == 1, "prologue load order");
+    // Q rows go through LDS with direct loads, into the four stages the
+    // prologue does not fill: K stage 3 and V stages 1..3 (groups of kG rows
+    // in the K/V layout). V stage 3 is also iteration 0's V(-1), which is
+    // multiplied by P(-1) = 0; Q rows are finite, so that adds zeros.
+    static_assert(C::kKStages == 4 && C::kVStages == 4, "Q staging stages");
+    constexpr int kQGroupsPerWave = C::kBlockM / G / C::kWaves;
+    auto q_group_off = [&](int g) __attribute__((always_inline)) {
+      return g < C::kGroups ? 3 * C::kTileBytes + g * GB
+                            : (C::kKStages + 1) * C::kTileBytes + (g - C::kGroups) * GB;
+    };
     issue_tile(kbase, kstage(0), 0);
-    issue_tile(vbase, vstage(-1), -1);
+    {
+      const int64_t qaddr = uniform_i64(reinterpret_cast<int64_t>(Q + tile.q_row0 * rs + int64_t(tile.head) * D));
+      const auto qrsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<__bf16*>(qaddr), 0,
+                                                           tile.q_rows * row_bytes, kBufferFlags);
+#pragma unroll
+      for (int i = 0; i < kQGroupsPerWave; ++i) {
+        const int g = wave * kQGroupsPerWave + i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            qrsrc, (void ZL_LDS*)(smem + q_group_off(g)), 16, ld_lane,
+            __builtin_amdgcn_readfirstlane(g * G * int(rs) * 2), 0, 0);
+      }
+    }
     issue_tile(kbase, kstage(1), 1);
     issue_tile(vbase, vstage(0), 0);
     issue_tile(kbase, kstage(2), 2);
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * kLoadsPerTile));  // K(0) landed
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * kLoadsPerTile));  // K(0) and Q landed
     lds_barrier();
+    {
+      // Q^T fragments: row qr, chunk 2*ds + half (the K fragment pattern)
+      const int g0 = (wave * 32) / G;
+      int qo = q_group_off(g0) + ((qr % 32) / G) * GB + (half * G + qr % G) * 16;
+      asm volatile("" : "+v"(qo));
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) qf[ds] = lds_read_b128(smem + qo + ds * 2 * G * 16);
+    }
     f32x16 s_a[KB], s_b[KB];
     bf16x8 p_a[KB][2], p_b[KB][2];
 #pragma unroll
