@@ -115,6 +115,33 @@ def test_backward_ragged_and_head_splits(d):
     gate.check()
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_key_tile_and_step_edges(d):
+    """Key counts around the dK/dV tile (256 keys, 32 per wave) and query
+    counts giving one to six 32-row steps of either parity, with every item
+    reading the same key/value rows so that the dK/dV atomics of all items
+    add up in the same rows."""
+    H = 2
+    rng = np.random.default_rng(40 + d)
+    kls = [255, 256, 257, 511, 512, 513]
+    qls = [31, 32, 33, 96, 160, 161]
+    items, q_off = [], 0
+    for ql, kl in zip(qls, kls):
+        items.append(W.Item(q_off, ql, 0, kl, 0, H))
+        q_off += ql
+    kv_rows = max(kls)
+    mk = lambda n: torch.from_numpy(rng.standard_normal((n, H, d)).astype(np.float32)).to(torch.bfloat16)
+    q, k, v, g = mk(q_off), mk(kv_rows), mk(kv_rows), mk(q_off)
+    dq, dk, dv = _run(items, q.cuda(), k.cuda(), v.cuda(), g.cuda(), H, d, n_slots=5)
+    rq, rk, rv = _oracle_all(items, q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                             g.double().numpy(), 1 / math.sqrt(d))
+    gate = Gate(f"tile edges d={d} backward")
+    gate.add("dQ", dq, rq)
+    gate.add("dK", dk, rk)
+    gate.add("dV", dv, rv)
+    gate.check()
+
+
 @pytest.mark.timeout(900)
 def test_backward_training_step_full_size():
     """Config 4 at full size: every image item in full on every head; the
