@@ -6,7 +6,7 @@ shares no code with the HIP path; the two meet only at the seeded inputs.
 
 What it follows
 ---------------
-* The engine runs whole sequences alongside distributed-attention shards
+* Short sequences run whole, side by side with the shards of split sequences
   (newx.sg page "Zellige: Moldable Sequence Placement for Mixed Image-Video
   DiT Training", Abstract). A shard is one split theta = (q, h, k) of a
   sequence's queries, heads and key/value states (pith.science review of

@@ -3,9 +3,9 @@
 TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call this module.
 
-The engine "stably schedules and fuses" whole sequences and shards on a
-shared rank (pith.science review of arXiv 2608.01150, "What carries the
-argument"). The pages give no algorithm; the reading taken here is a
+On one rank the engine places whole sequences and shards together, in a
+stable order, and runs them as one fused launch (pith.science review of
+arXiv 2608.01150, "What carries the argument"). The pages give no algorithm; the reading taken here is a
 stable longest-processing-time-first (LPT) list schedule:
 
 1. Cut every item into tiles of ``block_m`` query rows x one head, in the
