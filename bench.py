@@ -19,7 +19,10 @@ forward on the other workloads (the tiny check, images only, the KV-split
 shard with its merge, with and without the in-launch key split, and the two
 second-workload shares), and ``price_table`` gives the additivity ratios of
 the mixed rank share. Every GPU time comes from HIP events on the launch
-stream; medians and minima are reported beside the means. The cpu_baseline
+stream; medians and minima are reported beside the means. ``mfma_attainable``
+gives the rate of a register-only bf16 MFMA stream on this GPU, on random and
+on constant operands: the chip is power-limited, and the random figure is the
+matrix-core rate it attains on data like the workload's. The cpu_baseline
 leg times the fp64 oracle on a bounded sample of the same workload on the
 host cores (one thread per core, single-threaded BLAS).
 """
@@ -60,6 +63,10 @@ def _args():
                          "alone and per bucket, against the coalesced launch (additivity check)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (scale reference for FETCH/WRITE_SIZE)")
+    ap.add_argument("--calibrate-mfma", action="store_true",
+                    help="only time the register-only bf16 MFMA stream on random and constant operands")
+    ap.add_argument("--no-calib", action="store_true",
+                    help="leave the MFMA calibration out of the bench line")
     return ap.parse_args()
 
 
@@ -280,6 +287,17 @@ def _price_table(zl, wl, q, k, v, dev, n_slots):
             "data": "synthetic"}
 
 
+def _calibrate_mfma(zl, iters=400_000):
+    """Rate of a register-only stream of bf16 32x32x16 MFMAs on this GPU
+    (``zl_calib_mfma``), on random and on constant operands: under its power
+    limit the chip attains less than the nominal peak when the operand bits
+    switch, and the random figure is the ceiling a kernel on random data
+    meets on this GPU."""
+    return {"random_bf16": round(zl.calibrate_mfma("random", iters), 1),
+            "constant_bf16": round(zl.calibrate_mfma("constant", iters), 1),
+            "unit": "TFLOP/s", "iters": iters, "kernel": "mfma_stream"}
+
+
 def _bench_configs(zl, W, dev, stream, n_slots):
     """Forward time of the other workloads: the tiny check (microseconds),
     images only, the KV-split shard with its theta-k merge (with and without
@@ -362,6 +380,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n * 4}), flush=True)
         return
+    if a.calibrate_mfma:
+        print(json.dumps(_calibrate_mfma(zl)), flush=True)
+        return
     wl = W.config(a.config)
     inp = W.make_inputs(wl)
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
@@ -418,6 +439,10 @@ def main():
         "worklist_build_ms": round(wl_ms, 3),
     }
     print(f"[bench] headline forward: {sp}", file=sys.stderr, flush=True)
+    if not a.no_calib:
+        cal = _calibrate_mfma(zl)
+        cal["frac_of_random"] = round(achieved / cal["random_bf16"], 4)
+        out["mfma_attainable"] = cal
 
     if not a.no_price and a.config == 2:
         pt = _price_table(zl, wl, q, k, v, dev, n_slots)

@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libzl.so")
 
-DEVICE_SOURCES = ["zl_fwd.hip", "zl_merge.hip", "zl_bwd.hip"]
+DEVICE_SOURCES = ["zl_fwd.hip", "zl_merge.hip", "zl_bwd.hip", "zl_calib.hip"]
 HOST_SOURCES = ["zl_host.cpp"]
 
 # Flags of the host object. The host code validates floats (a NaN softmax

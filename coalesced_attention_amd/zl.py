@@ -23,10 +23,11 @@ STATUS = {0: "ZL_OK", -1: "ZL_ERR_NULL", -2: "ZL_ERR_SHAPE", -3: "ZL_ERR_RANGE",
           -7: "ZL_ERR_WORKLIST", -8: "ZL_ERR_HIP", -9: "ZL_ERR_ARG"}
 WORKLIST_MAGIC = 0x31574C5A
 
-# Symbols include/zl.h declares (checked by the CPU tests).
+# Symbols include/zl.h and include/zl_calib.h declare (checked by the CPU tests).
 EXPORTS = ("zl_abi_version", "zl_status_string", "zl_last_error", "zl_build_worklist",
            "zl_coalesced_attn_fwd", "zl_merge_partials", "zl_coalesced_attn_bwd",
-           "zl_coalesced_attn_fwd_noalloc")
+           "zl_coalesced_attn_fwd_noalloc", "zl_calib_mfma")
+CALIB_OPERANDS = {"random": 0, "constant": 1}
 # Device scratch the allocation-free forward holds per GPU (ZL_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -112,6 +113,8 @@ def _load() -> ctypes.CDLL:
     lib.zl_coalesced_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, fp, fp, vp]
     lib.zl_coalesced_attn_bwd.restype = ctypes.c_int
     lib.zl_coalesced_attn_bwd.argtypes = [vp, vp, vp, vp, vp, fp, fp, vp, fp, fp, fp, fp, vp]
+    lib.zl_calib_mfma.restype = ctypes.c_int
+    lib.zl_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double), vp]
     return lib
 
 
@@ -379,3 +382,18 @@ def merge_partials(o, lse, row0: int, n_parts: int, rows: int, part_row_stride: 
                                  part_row_stride, o_out.data_ptr(), lse_out.data_ptr(),
                                  _stream_handle(stream, o.device)), "zl_merge_partials")
     return o_out, lse_out
+
+
+def calibrate_mfma(operands: str = "random", iters: int = 400_000, stream=None) -> float:
+    """TFLOP/s of a register-only stream of bf16 32x32x16 MFMAs on the current
+    GPU with the given operand kind ("random" or "constant"): the rate this
+    GPU attains under its power limit, for context beside a kernel's rate.
+    Synchronous."""
+    import torch
+    if operands not in CALIB_OPERANDS:
+        raise ValueError(f"operands must be one of {sorted(CALIB_OPERANDS)}")
+    dev = torch.device("cuda", torch.cuda.current_device())
+    out = ctypes.c_double(0.0)
+    _check(lib.zl_calib_mfma(CALIB_OPERANDS[operands], int(iters), ctypes.byref(out),
+                             _stream_handle(stream, dev)), "zl_calib_mfma")
+    return out.value

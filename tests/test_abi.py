@@ -1,4 +1,4 @@
-"""The C-ABI library on the CPU: it loads, exports what include/zl.h declares,
+"""The C-ABI library on the CPU: it loads, exports what include/*.h declare,
 its worklist equals the reference LPT schedule bit for bit, and every
 argument error is rejected on the host before any HIP call."""
 
@@ -15,12 +15,16 @@ from oracle.worklist import lpt_schedule, lpt_schedule_bwd, split_plan
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "zl.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(zl_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b(zl_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
@@ -193,6 +197,19 @@ def test_fwd_and_merge_reject_bad_arguments_before_any_hip_call():
     assert m(2, 10, 4, 0, 4, 128, p + 4, p, 10, p, p, None) == -6
     q = 1 << 30
     assert m(2, 10, 4, 0, 4, 128, p, q, 10, p, q + (1 << 24), None) == -9   # output overlaps parts
+
+
+def test_mfma_calibration_rejects_bad_arguments_before_any_hip_call():
+    c = zl.lib.zl_calib_mfma
+    out = ctypes.c_double(0.0)
+    assert c(0, 1000, None, None) == -1
+    assert c(2, 1000, ctypes.byref(out), None) == -9
+    assert c(-1, 1000, ctypes.byref(out), None) == -9
+    assert c(0, 0, ctypes.byref(out), None) == -9
+    assert c(1, (1 << 24) + 1, ctypes.byref(out), None) == -9
+    assert out.value == 0.0
+    with pytest.raises(ValueError):
+        zl.calibrate_mfma("zeros")
 
 
 def test_nan_and_oversized_shapes_are_rejected_by_the_shipped_library():
