@@ -487,6 +487,14 @@ def main():
         out["configs"] = _bench_configs(zl, W, dev, stream, n_slots)
         print(f"[bench] configs done", file=sys.stderr, flush=True)
 
+    if "mfma_attainable" in out:  # every MFMA rate beside this GPU's random-operand ceiling
+        ceil = out["mfma_attainable"]["random_bf16"]
+        if "backward" in out:
+            out["backward"]["frac_of_random"] = round(out["backward"]["TFLOP/s"] / ceil, 4)
+        for rec in out.get("configs", {}).values():
+            if "TFLOP/s" in rec:
+                rec["frac_of_random"] = round(rec["TFLOP/s"] / ceil, 4)
+
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(wl, inp, a.cpu_seconds)
     print(json.dumps(out), flush=True)
