@@ -478,6 +478,18 @@ def main():
                         "frac_of_hbm_peak": round(mbytes / (mms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                         "bytes": mbytes, "traffic": measured_traffic("merge_kernel<128>")}
         del po, pl, mo, ml
+        # a plain device copy of 1 GiB on the same GPU: the HBM rate a
+        # streaming kernel attains here, beside the merge's
+        src = torch.ones(1 << 28, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        cms = float(np.median(_launch_ms(lambda: dst.copy_(src), 5, stream)))
+        copy_gbps = 2 * (1 << 30) / (cms * 1e-3) / 1e9
+        out["merge"]["copy_GB/s"] = round(copy_gbps, 1)
+        out["merge"]["frac_of_copy"] = round(mbytes / (mms * 1e-3) / 1e9 / copy_gbps, 4)
+        del src, dst
 
     if not a.no_bwd:
         out["backward"] = _bench_backward(zl, W, dev, stream, n_slots)
