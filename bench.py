@@ -301,12 +301,15 @@ def _calibrate_mfma(zl, iters=400_000):
 def _bench_configs(zl, W, dev, stream, n_slots):
     """Forward time of the other workloads: the tiny check (microseconds),
     images only, the KV-split shard with its theta-k merge (with and without
-    the in-launch key split), and the two second-workload shares. HIP events
+    the in-launch key split), and the two second-workload shares (with and
+    without splitting their long items into key chunks of at most 65,536
+    keys, merged inside the launch). HIP events
     around each launch; ~20 launches after 3 warm-ups (fewer on the long
     ones)."""
     import torch
     out = {}
-    for c, kv_chunk in ((0, 0), (1, 0), (3, 0), (3, 27456), (5, 0), (6, 0)):
+    for c, kv_chunk in ((0, 0), (1, 0), (3, 0), (3, 27456), (3, 65536), (5, 0), (5, 65536), (6, 0),
+                        (6, 65536)):
         wl = W.config(c)
         inp = W.make_inputs(wl)
         q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
