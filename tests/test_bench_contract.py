@@ -34,3 +34,14 @@ def test_traffic_is_reported_only_for_the_profiled_sources(tmp_path, monkeypatch
     assert bench.measured_traffic("merge_kernel<128>") is None
     src.write_text("kernel v2\n")  # the kernel changed after its counters were taken
     assert bench.measured_traffic("fwd_kernel<128>") is None
+
+
+def test_committed_traffic_records_match_the_committed_kernel_sources():
+    """profiles/traffic.json was taken on the kernels as they are: every
+    record's source hash matches, so the bench line reports its traffic."""
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
+        recs = json.load(fh)
+    assert recs
+    for kernel, rec in recs.items():
+        assert rec["source_sha256"] == bench.kernel_source_hash(rec["sources"]), kernel
+        assert bench.measured_traffic(kernel) == rec["fetch_bytes"] + rec["write_bytes"]
