@@ -17,9 +17,17 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-# Gradient gates: the forward's absolute bounds plus a per-tensor relative
-# L2 error (gradients of long items are small).
+# Gradient gates: the forward's bounds plus a per-tensor relative L2 error
+# (gradients of long items are small). A gradient row (one query's dQ, one
+# key's dK or dV, over head_dim) is a sum of terms that share one bf16
+# coefficient per query or key (dS or P, rounded to ~2^-9 relative), so
+# every element of the row carries an error in proportion to the row's
+# terms, also an element that cancels to near zero. The max-abs bound
+# therefore applies as |got - ref| <= MAX_ABS + MAX_REL * max|ref row|: keys
+# that many queries attend to reach rows of |dK|, |dV| up to 15-20, where
+# 2e-2 absolute would be a 1e-3 relative bound.
 MAX_ABS = 2e-2
+MAX_REL = 1e-2
 MEAN_ABS = 2e-3
 REL_L2 = 1e-2
 
@@ -49,7 +57,8 @@ class Gate:
     def add(self, name, got, ref):
         d = np.abs(got - ref)
         s = self.stats.setdefault(name, [0.0, 0.0, 0, 0.0, 0.0])
-        s[0] = max(s[0], float(d.max(initial=0.0)))
+        row = np.abs(ref).max(axis=-1, keepdims=True)
+        s[0] = max(s[0], float((d - MAX_REL * row).max(initial=0.0)))
         s[1] += float(d.sum())
         s[2] += d.size
         s[3] += float((d ** 2).sum())
@@ -60,7 +69,8 @@ class Gate:
         for name, (mx, sm, n, num, den) in self.stats.items():
             mean = sm / max(1, n)
             rel = math.sqrt(num / den) if den > 0 else math.sqrt(num)
-            log(f"{self.what} {name}: max_abs={mx:.3e} mean_abs={mean:.3e} rel_l2={rel:.3e}")
+            log(f"{self.what} {name}: max(|d| - {MAX_REL} max|ref row|)={mx:.3e} mean_abs={mean:.3e} "
+                f"rel_l2={rel:.3e}")
             if not (mx <= MAX_ABS and mean <= MEAN_ABS and rel <= REL_L2):
                 bad.append((name, mx, mean, rel))
         assert not bad, (self.what, bad)
