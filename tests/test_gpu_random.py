@@ -62,14 +62,16 @@ def _random_problem(rng):
 GRAD_MAX_REL = 1e-2
 
 
-def _gates(name, got, ref, rel_tol=0.0):
+def _gates(name, got, ref, rel_tol=0.0, absolute=True):
     d = np.abs(got - ref)
     row = np.abs(ref).max(axis=-1, keepdims=True) if ref.size else ref
     mx = float((d - rel_tol * row).max(initial=0.0))
     mean = float(d.mean()) if d.size else 0.0
     den = float(np.linalg.norm(ref))
     rel = float(np.linalg.norm(got - ref)) / den if den > 0 else float(np.linalg.norm(got - ref))
-    assert mx <= MAX_ABS and mean <= MEAN_ABS and rel <= REL_L2, (name, mx, mean, rel)
+    assert rel <= REL_L2, (name, mx, mean, rel)
+    if absolute:
+        assert mx <= MAX_ABS and mean <= MEAN_ABS, (name, mx, mean, rel)
     return mx, rel
 
 
@@ -147,11 +149,22 @@ def test_larger_random_worklists_forward_and_backward_against_oracle(seed):
     items, q_rows, kv_rows, H, d = _larger_problem(rng)
     n_slots = int(rng.choice([0, 256]))
     kv_chunk = int(rng.choice([0, 1024]))
+    # Sharper softmax rows on some tables: scores spread over tens of units.
+    # O and LSE keep every gate. The gradients (8x larger with Q) keep the
+    # relative L2 gate but not the absolute ones: the method's
+    # D = rowsum(dO * O) takes the forward's
+    # O, whose dominant weight carries its bf16 rounding (~2^-9 of V) when the
+    # row's shift is not its maximum, and where dP - D cancels in a sharp row
+    # that error dominates the gradient row (up to ~60% of a row whose terms
+    # are much larger than the row itself; the tensors stay at ~4e-3 relative
+    # L2, and with D taken from the same O the rows match to ~2e-3).
+    qscale = float(rng.choice([1.0, 3.0, 8.0]))
     log(f"larger seed {seed}: {len(items)} items, q_rows {q_rows}, kv_rows {kv_rows}, H {H}, d {d}, "
-        f"n_slots {n_slots}, kv_chunk {kv_chunk}")
+        f"n_slots {n_slots}, kv_chunk {kv_chunk}, q scale {qscale}")
     g = torch.Generator().manual_seed(100 + seed)
     mk = lambda n: torch.randn((n, H, d), generator=g).to(torch.bfloat16)
     q, k, v, do = mk(q_rows), mk(kv_rows), mk(kv_rows), mk(q_rows)
+    q = (q.float() * qscale).to(torch.bfloat16)
     dev = torch.device("cuda:0")
     wl = zl.build_worklist(items, q_rows, kv_rows, H, d, n_slots=n_slots, device=dev, kv_chunk=kv_chunk)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
@@ -167,4 +180,4 @@ def test_larger_random_worklists_forward_and_backward_against_oracle(seed):
                               orc.coalesced_backward(Qh, Kh, Vh, Gh, items, s)):
         got = got.cpu().numpy()
         assert np.isfinite(got).all(), name
-        _gates(name, got, ref, GRAD_MAX_REL)
+        _gates(name, got, ref, GRAD_MAX_REL, absolute=qscale == 1.0)
