@@ -411,10 +411,15 @@ def main():
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
+    # the timed steps run back to back, with nothing between the launches;
+    # a second pass brackets each launch with its own pair of HIP events for
+    # the per-launch spread and the kernel time of the roofline
     t0 = time.perf_counter()
-    launch_ms = _launch_ms(step, a.steps, stream)
+    for _ in range(a.steps):
+        step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    launch_ms = _launch_ms(step, a.steps, stream)
     sp = _spread(launch_ms)
     kern_ms = sp["ms_mean"]
 
