@@ -302,14 +302,14 @@ def _bench_configs(zl, W, dev, stream, n_slots):
     """Forward time of the other workloads: the tiny check (microseconds),
     images only, the KV-split shard with its theta-k merge (with and without
     the in-launch key split), and the two second-workload shares (with and
-    without splitting their long items into key chunks of at most 65,536
-    keys, merged inside the launch). HIP events
+    without the automatic key split, which cuts their long items into
+    chunks of at most 65,536 keys merged inside the launch). HIP events
     around each launch; ~20 launches after 3 warm-ups (fewer on the long
     ones)."""
     import torch
     out = {}
-    for c, kv_chunk in ((0, 0), (1, 0), (3, 0), (3, 27456), (3, 65536), (5, 0), (5, 65536), (6, 0),
-                        (6, 65536)):
+    for c, kv_chunk in ((0, 0), (1, 0), (3, 0), (3, 27456), (3, 65536), (5, 0), (5, zl.KV_CHUNK_AUTO),
+                        (6, 0), (6, zl.KV_CHUNK_AUTO)):
         wl = W.config(c)
         inp = W.make_inputs(wl)
         q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
@@ -354,7 +354,8 @@ def _bench_configs(zl, W, dev, stream, n_slots):
             if c != 0:
                 rec["with_merge"] = {"ms_median": spm["ms_median"], "ms_min": spm["ms_min"],
                                      "TFLOP/s": round(F / (spm["ms_median"] * 1e-3) / 1e12, 2)}
-        out[f"{c}" if kv_chunk == 0 else f"{c}_kv_chunk_{kv_chunk}"] = rec
+        out[f"{c}" if kv_chunk == 0 else
+            f"{c}_kv_chunk_{'auto' if kv_chunk == zl.KV_CHUNK_AUTO else kv_chunk}"] = rec
         del q, k, v, o, lse, ws, built
         torch.cuda.empty_cache()
     return out

@@ -63,7 +63,7 @@ int check_worklist(const void* h_wl, const zl_worklist_header** hdr) {
     if (h->bwd_slots_offset < need) return fail(ZL_ERR_WORKLIST, "worklist sections overlap");
     need = h->bwd_slots_offset + uint64_t(h->n_slots + 1) * sizeof(int32_t);
   }
-  if (h->kv_chunk < 0 || h->n_vitems < h->n_items || h->n_merges < 0 || h->n_dq_tiles < 0 ||
+  if (h->kv_chunk < ZL_KV_CHUNK_AUTO || h->n_vitems < h->n_items || h->n_merges < 0 || h->n_dq_tiles < 0 ||
       h->ws_rows < 0 || (h->n_merges > 0) != (h->ws_rows > 0))
     return fail(ZL_ERR_WORKLIST, "worklist split fields out of range");
   if (h->outmap_offset < need) return fail(ZL_ERR_WORKLIST, "worklist sections overlap");
@@ -228,7 +228,8 @@ extern "C" int zl_build_worklist(const zl_problem* problem, const zl_item* items
     return fail(ZL_ERR_SHAPE, "head_dim must be 64 or 128 and sizes non-negative");
   if (int64_t(p.num_heads) * p.head_dim > kMaxRowElems)
     return fail(ZL_ERR_SHAPE, "num_heads * head_dim exceeds %lld", (long long)kMaxRowElems);
-  if (p.kv_chunk < 0) return fail(ZL_ERR_ARG, "problem.kv_chunk must be >= 0");
+  if (p.kv_chunk < ZL_KV_CHUNK_AUTO)
+    return fail(ZL_ERR_ARG, "problem.kv_chunk must be >= 0 or ZL_KV_CHUNK_AUTO");
   if (!(p.softmax_scale <= 0.f || std::isfinite(p.softmax_scale)))
     return fail(ZL_ERR_ARG, "softmax_scale must be finite");
   int rc = validate_items(p, items, n_items);
@@ -250,8 +251,13 @@ extern "C" int zl_build_worklist(const zl_problem* problem, const zl_item* items
     const zl_item& it = items[i];
     const int64_t qblocks = (int64_t(it.q_len) + block_m - 1) / block_m;
     n_unsplit64 += int64_t(it.head_cnt) * qblocks;
-    if (p.kv_chunk > 0 && it.q_len > 0 && it.head_cnt > 0 && it.kv_len > p.kv_chunk) {
-      const int64_t n = (int64_t(it.kv_len) + p.kv_chunk - 1) / p.kv_chunk;
+    // ZL_KV_CHUNK_AUTO: only items above the automatic threshold, in chunks
+    // of at most ZL_KV_CHUNK_AUTO_KEYS keys
+    const int32_t kc = p.kv_chunk != ZL_KV_CHUNK_AUTO ? p.kv_chunk
+                       : it.kv_len > ZL_KV_CHUNK_AUTO_MIN_KEYS ? ZL_KV_CHUNK_AUTO_KEYS
+                                                               : 0;
+    if (kc > 0 && it.q_len > 0 && it.head_cnt > 0 && it.kv_len > kc) {
+      const int64_t n = (int64_t(it.kv_len) + kc - 1) / kc;
       const int64_t c = ((int64_t(it.kv_len) + n - 1) / n + 63) / 64 * 64;
       parts[size_t(i)] = int32_t((it.kv_len + c - 1) / c);
       chunk[size_t(i)] = int32_t(c);

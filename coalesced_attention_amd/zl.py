@@ -28,6 +28,9 @@ EXPORTS = ("zl_abi_version", "zl_status_string", "zl_last_error", "zl_build_work
            "zl_coalesced_attn_fwd", "zl_merge_partials", "zl_coalesced_attn_bwd",
            "zl_coalesced_attn_fwd_noalloc", "zl_calib_mfma")
 CALIB_OPERANDS = {"random": 0, "constant": 1}
+# kv_chunk value that splits only the items with more than 131,072 keys, into
+# chunks of at most 65,536 keys (ZL_KV_CHUNK_AUTO)
+KV_CHUNK_AUTO = -1
 # Device scratch the allocation-free forward holds per GPU (ZL_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -224,7 +227,9 @@ def build_worklist(items: Iterable, q_rows: int, kv_rows: int, num_heads: int, h
     """zl_build_worklist. ``items`` are (q_off, q_len, kv_off, kv_len,
     head_begin, head_cnt) tuples or objects with ``as_tuple()``. With
     ``device`` the worklist is also copied there; ``kv_chunk`` > 0 splits
-    items with more keys into key chunks merged inside the forward."""
+    items with more keys into key chunks merged inside the forward, and
+    ``KV_CHUNK_AUTO`` splits only items with more than 131,072 keys, into
+    chunks of at most 65,536."""
     arr, n = _items_array(items)
     prob = Problem(q_rows, kv_rows, num_heads, head_dim, softmax_scale, kv_chunk)
     nbytes = ctypes.c_size_t(0)

@@ -86,14 +86,21 @@ typedef struct zl_item {
  * partials are then merged exactly as zl_merge_partials does (a theta k
  * split done inside one rank: pith.science review, "What carries the
  * argument"). This shortens the longest tiles, so the static schedule
- * balances better. kv_chunk = 0: no split. */
+ * balances better. kv_chunk = 0: no split.
+ * kv_chunk = ZL_KV_CHUNK_AUTO splits only the items with more than
+ * ZL_KV_CHUNK_AUTO_MIN_KEYS keys, each into chunks of at most
+ * ZL_KV_CHUNK_AUTO_KEYS keys (as kv_chunk = ZL_KV_CHUNK_AUTO_KEYS would);
+ * shorter items stay whole. */
+#define ZL_KV_CHUNK_AUTO (-1)
+#define ZL_KV_CHUNK_AUTO_MIN_KEYS 131072
+#define ZL_KV_CHUNK_AUTO_KEYS 65536
 typedef struct zl_problem {
   int64_t q_rows;
   int64_t kv_rows;
   int32_t num_heads;
   int32_t head_dim;
   float softmax_scale;
-  int32_t kv_chunk; /* >= 0 */
+  int32_t kv_chunk; /* >= 0, or ZL_KV_CHUNK_AUTO */
 } zl_problem;
 
 /* Worklist buffer = header, then sections at the header's offsets (each
@@ -207,7 +214,8 @@ const char* zl_last_error(void);
  * Errors: ZL_ERR_NULL, ZL_ERR_SHAPE (head_dim not 64 or 128, num_heads < 1,
  * num_heads * head_dim > 2^20, negative row counts), ZL_ERR_RANGE,
  * ZL_ERR_OVERLAP, ZL_ERR_BUFSIZE, ZL_ERR_ARG (n_items < 0, n_slots < 0 or
- * > 1<<20, kv_chunk < 0, softmax_scale NaN or infinite).
+ * > 1<<20, kv_chunk < 0 other than ZL_KV_CHUNK_AUTO, softmax_scale NaN or
+ * infinite).
  * The schedule is a stable LPT list schedule: the reading taken of the
  * engine's stable scheduling of whole sequences and shards on one rank
  * (pith.science review of arXiv 2608.01150, "What carries the argument"). */
@@ -273,7 +281,7 @@ int zl_coalesced_attn_bwd(const void* h_wl, const void* d_wl, const void* q, con
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc). Same computation, arguments and errors as
  * zl_coalesced_attn_fwd, except that the key-chunk partials of a worklist
- * built with kv_chunk > 0 go to a scratch array that the library holds in
+ * built with a key split go to a scratch array that the library holds in
  * device memory (ZL_NOALLOC_SCRATCH_BYTES on each GPU it runs on, kept until
  * the process ends) instead of a caller workspace. It calls no hipMalloc,
  * hipFree or allocating routine.

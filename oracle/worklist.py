@@ -27,7 +27,9 @@ Key split inside a launch (a theta k split of one item on one rank, same
 section): with ``kv_chunk`` > 0 an item with queries and more than
 kv_chunk keys is cut into n = ceil(kv_len / kv_chunk) key chunks of
 ceil(kv_len / n) keys rounded up to a multiple of 64 (the last chunk
-shorter; n then recounted). Chunk p of the k-th split item (in item order)
+shorter; n then recounted). With ``kv_chunk`` = -1 (automatic) only items
+with more than 131,072 keys are cut, as by kv_chunk = 65,536 (the threshold
+and chunk size are this build's choice, not the pages'). Chunk p of the k-th split item (in item order)
 is numbered n_items + (chunks of earlier split items) + p; its tiles are cut
 after all unsplit items' tiles, in (chunk, head, query block) order, and
 its partial output goes to workspace rows ws_row0 + p * q_len, ws_row0
@@ -56,9 +58,17 @@ def _tuple(it):
     return it.as_tuple() if hasattr(it, "as_tuple") else tuple(int(x) for x in it)
 
 
+# kv_chunk = -1 (automatic): items with more than AUTO_MIN_KEYS keys are
+# split as by kv_chunk = AUTO_KEYS, shorter ones stay whole
+AUTO_MIN_KEYS = 131072
+AUTO_KEYS = 65536
+
+
 def split_parts(q_len: int, kv_len: int, head_cnt: int, kv_chunk: int) -> Tuple[int, int]:
     """(number of key chunks, keys per chunk) of one item; (1, 0) when the
     item is not split."""
+    if kv_chunk == -1:
+        kv_chunk = AUTO_KEYS if kv_len > AUTO_MIN_KEYS else 0
     if kv_chunk <= 0 or q_len <= 0 or head_cnt <= 0 or kv_len <= kv_chunk:
         return 1, 0
     n = -(-kv_len // kv_chunk)

@@ -83,7 +83,8 @@ def _tile_array(tiles):
 
 
 @pytest.mark.parametrize("cfg,kv_chunk,n_slots", [(0, 64, 0), (0, 64, 3), (0, 100, 7), (2, 8192, 256),
-                                                  (3, 27456, 256), (3, 40000, 97), (3, 1 << 20, 256)])
+                                                  (3, 27456, 256), (3, 40000, 97), (3, 1 << 20, 256),
+                                                  (3, -1, 256), (5, -1, 256), (6, -1, 97)])
 def test_key_split_worklist_matches_reference(cfg, kv_chunk, n_slots):
     wl = W.config(cfg)
     built = zl.build_worklist(wl.items, wl.q_rows, wl.kv_rows, wl.num_heads, wl.head_dim,
@@ -145,7 +146,8 @@ def test_build_errors():
     assert _rc_build([(0, 10, 0, 10, 0, 2), (5, 10, 0, 10, 2, 2)]) == 0    # disjoint heads
     assert _rc_build([(0, 10, 0, 10, 0, 4), (10, 10, 0, 10, 0, 4)]) == 0   # adjacent rows
     assert _rc_build(ok, n_slots=-1) == -9
-    assert _rc_build(ok, kv_chunk=-1) == -9
+    assert _rc_build(ok, kv_chunk=-2) == -9
+    assert _rc_build(ok, kv_chunk=-1) == 0  # ZL_KV_CHUNK_AUTO
     assert _rc_build(ok, kv_chunk=1) == 0
     assert _rc_build(ok, nbytes=64) == -5
     assert _rc_build(ok, scale=float("inf")) == -9

@@ -44,12 +44,14 @@ def _host(x):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("c,kv_chunk", [(0, 0), (1, 0), (2, 0), (3, 0), (0, 64), (3, 27456), (5, 0),
-                                        (6, 0), (6, 65536)])
+                                        (6, 0), (6, 65536), (5, -1)])
 def test_forward_parity(c, kv_chunk):
     """Every config against the oracle; with kv_chunk > 0 the long items are
     split into key chunks inside the launch and merged (config 3's 109,800
     keys into 4 chunks of 27,456; the 1080p shard's 334,560 keys into 6
-    chunks of at most 65,536; config 0's items into 64-key chunks)."""
+    chunks of at most 65,536; the four-720p share's 147,600 keys into 3
+    chunks by the automatic split, kv_chunk = -1; config 0's items into
+    64-key chunks)."""
     wl, inp, (q, k, v) = _workload(c)
     log(f"config {c}: forward on GPU, {len(wl.items)} items, kv_chunk {kv_chunk}")
     built, o, lse = run_fwd(wl.items, q, k, v, wl.num_heads, wl.head_dim, kv_chunk=kv_chunk)

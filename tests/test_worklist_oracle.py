@@ -96,7 +96,7 @@ def test_backward_tiles_cover_every_key_head_pair_once():
     assert loads == [sum(t.cost for t in tiles[begin[s]:begin[s + 1]]) for s in range(5)]
 
 
-@pytest.mark.parametrize("cfg,kv_chunk", [(0, 64), (0, 100), (3, 27456)])
+@pytest.mark.parametrize("cfg,kv_chunk", [(0, 64), (0, 100), (3, 27456), (6, -1)])
 def test_key_split_covers_every_key_once(cfg, kv_chunk):
     """With a key split every (query row, head, key) triple of every item is
     still covered by exactly one forward tile, and each item's chunk tiles
@@ -118,7 +118,7 @@ def test_key_split_covers_every_key_once(cfg, kv_chunk):
                 vit[v] = idx
                 v += 1
     assert v == len(outmap)
-    if cfg == 3:
+    if cfg in (3, 6):
         # count (row-block, head, key) coverage per item by key ranges only
         for idx, it in enumerate(items):
             q_off, q_len, kv_off, kv_len, h0, hc = it
